@@ -1,0 +1,146 @@
+"""Seeded synthetic inputs for the mixer core.
+
+Both the GPU path and the CPU oracle consume exactly these arrays, so this
+module is the only code the two share. It holds the input distributions and
+nothing of the method's arithmetic:
+
+  q, k, v, x, B, C, z, D ~ N(0, 1)
+  delta = softplus(N(-2, 0.5))          (already >= 0; no dt bias downstream)
+  A     = -exp(N(0, 0.5))               (real, negative, per channel and state)
+  conv_w ~ N(0, 1) / sqrt(K), conv_b ~ 0.1 N(0, 1)
+  beta_a, beta_s ~ 1 + 0.1 N(0, 1)
+
+The second argument of N(.,.) is a standard deviation. Draws are float64 from
+numpy's PCG64 in a fixed order, then cast: activations to bfloat16 (round to
+nearest even) for bf16 workloads or to float32 for f32 workloads; parameters
+and recurrent states always to float32.  Arrays are returned as float32 whose
+values are exactly representable in the workload dtype, plus helpers that give
+the bf16 bit pattern for upload.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .configs import MixerShape
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """uint16 bit pattern of float32 values that are already bf16-representable."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return (a.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _act(a: np.ndarray, dtype: str) -> np.ndarray:
+    a = a.astype(np.float32)
+    return bf16_round(a) if dtype == "bf16" else a
+
+
+def _softplus(a: np.ndarray) -> np.ndarray:
+    return np.log1p(np.exp(a))
+
+
+def _params(rng: np.random.Generator, Di: int, Ns: int, K: int) -> dict:
+    A = (-np.exp(rng.normal(0.0, 0.5, size=(Di, Ns)))).astype(np.float32)
+    D = rng.standard_normal(Di).astype(np.float32)
+    conv_w = (rng.standard_normal((Di, K)) / np.sqrt(K)).astype(np.float32)
+    conv_b = (0.1 * rng.standard_normal(Di)).astype(np.float32)
+    beta_a = (1.0 + 0.1 * rng.standard_normal(Di)).astype(np.float32)
+    beta_s = (1.0 + 0.1 * rng.standard_normal(Di)).astype(np.float32)
+    return dict(A=A, D=D, conv_w=conv_w, conv_b=conv_b, beta_a=beta_a, beta_s=beta_s)
+
+
+def prefill_inputs(shape: MixerShape, seed=0, layer: int | None = None) -> dict:
+    """One layer's prefill inputs over X~ = [meta; tokens] (length T = M + N).
+
+    Draw order: q, k, v, x, delta, B, C, z, then the parameters A, D, conv_w,
+    conv_b, beta_a, beta_s. A stack layer uses the seed sequence [seed, layer].
+    """
+    rng = np.random.default_rng(seed if layer is None else [seed, layer])
+    B, T, dt = shape.B, shape.T, shape.dtype
+    out = {}
+    out["q"] = _act(rng.standard_normal((B, T, shape.Hq, shape.Dh)), dt)
+    out["k"] = _act(rng.standard_normal((B, T, shape.Hkv, shape.Dh)), dt)
+    out["v"] = _act(rng.standard_normal((B, T, shape.Hkv, shape.Dh)), dt)
+    out["x"] = _act(rng.standard_normal((B, T, shape.Di)), dt)
+    out["delta"] = _act(_softplus(rng.normal(-2.0, 0.5, size=(B, T, shape.Di))), dt)
+    out["Bm"] = _act(rng.standard_normal((B, T, shape.Ns)), dt)
+    out["Cm"] = _act(rng.standard_normal((B, T, shape.Ns)), dt)
+    out["z"] = _act(rng.standard_normal((B, T, shape.Di)), dt)
+    out.update(_params(rng, shape.Di, shape.Ns, shape.K))
+    return out
+
+
+def decode_inputs(shape: MixerShape, seed=0) -> dict:
+    """Inputs of one decode token through an adjacent pair of layers.
+
+    Draw order: the shared cache (K already rotated, then V), then for layer
+    "a" (producer) and layer "b" (consumer) in turn: q, [k_new, v_new for the
+    producer only], x, delta, B, C, z, conv_state, ssm_state, then parameters.
+    The cache holds n_meta + cache_slots rows per sequence.
+    """
+    rng = np.random.default_rng(seed)
+    B, dt = shape.B, shape.dtype
+    S = shape.M + shape.cache_slots
+    out = {
+        "k_cache": _act(rng.standard_normal((B, S, shape.Hkv, shape.Dh)), dt),
+        "v_cache": _act(rng.standard_normal((B, S, shape.Hkv, shape.Dh)), dt),
+    }
+    for name in ("a", "b"):
+        d = {"q": _act(rng.standard_normal((B, shape.Hq, shape.Dh)), dt)}
+        if name == "a":
+            d["k_new"] = _act(rng.standard_normal((B, shape.Hkv, shape.Dh)), dt)
+            d["v_new"] = _act(rng.standard_normal((B, shape.Hkv, shape.Dh)), dt)
+        d["x"] = _act(rng.standard_normal((B, shape.Di)), dt)
+        d["delta"] = _act(_softplus(rng.normal(-2.0, 0.5, size=(B, shape.Di))), dt)
+        d["Bm"] = _act(rng.standard_normal((B, shape.Ns)), dt)
+        d["Cm"] = _act(rng.standard_normal((B, shape.Ns)), dt)
+        d["z"] = _act(rng.standard_normal((B, shape.Di)), dt)
+        d["conv_state"] = rng.standard_normal((B, shape.Di, shape.K - 1)).astype(np.float32)
+        d["ssm_state"] = rng.standard_normal((B, shape.Di, shape.Ns)).astype(np.float32)
+        d.update(_params(rng, shape.Di, shape.Ns, shape.K))
+        out[name] = d
+    return out
+
+
+def prefill_inputs_torch(shape: MixerShape, seed: int, layer: int, device):
+    """Device-side generator for the large stack workload (same distributions,
+    torch's Philox stream instead of PCG64; activations rounded to bf16).
+
+    Returns torch tensors on `device`. The oracle checks sampled outputs of
+    these by copying them to the host, so both sides still see the same bytes.
+    """
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + int(layer))
+    B, T = shape.B, shape.T
+    act = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+
+    def n(*s):
+        return torch.randn(*s, generator=g, device=device, dtype=torch.float32)
+
+    out = {}
+    out["q"] = n(B, T, shape.Hq, shape.Dh).to(act)
+    out["k"] = n(B, T, shape.Hkv, shape.Dh).to(act)
+    out["v"] = n(B, T, shape.Hkv, shape.Dh).to(act)
+    out["x"] = n(B, T, shape.Di).to(act)
+    out["delta"] = torch.nn.functional.softplus(n(B, T, shape.Di) * 0.5 - 2.0).to(act)
+    out["Bm"] = n(B, T, shape.Ns).to(act)
+    out["Cm"] = n(B, T, shape.Ns).to(act)
+    out["z"] = n(B, T, shape.Di).to(act)
+    Di, Ns, K = shape.Di, shape.Ns, shape.K
+    out["A"] = -torch.exp(n(Di, Ns) * 0.5)
+    out["D"] = n(Di)
+    out["conv_w"] = n(Di, K) / float(np.sqrt(K))
+    out["conv_b"] = 0.1 * n(Di)
+    out["beta_a"] = 1.0 + 0.1 * n(Di)
+    out["beta_s"] = 1.0 + 0.1 * n(Di)
+    return out
