@@ -1,0 +1,280 @@
+"""torch-facing wrappers of the libhm C ABI (argument marshalling only).
+
+Every function takes contiguous CUDA (HIP) tensors, passes their device
+pointers and the current stream to the library, and raises HmError with the
+library's message on any non-zero status.  Workspaces are allocated here with
+torch (the library itself never allocates).
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import HM_BF16, HM_F32, HmError, PrefillArgs, StepArgs, lib
+
+__all__ = [
+    "swa_meta_attn", "causal_conv1d", "selective_scan", "conv_selective_scan",
+    "branch_norm_mean", "mixer_prefill", "PrefillPlan", "mixer_step", "StepPlan",
+    "debug_attn_mask", "debug_tile_plan", "debug_attn_tiles", "debug_cache_slot",
+    "dtype_code",
+]
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return HM_BF16
+    if t.dtype == torch.float32:
+        return HM_F32
+    raise TypeError(f"unsupported activation dtype {t.dtype}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int):
+    if status != 0:
+        raise HmError(status, lib.hm_last_error().decode())
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libhm takes device tensors")
+        if not t.is_contiguous():
+            raise ValueError("libhm takes contiguous tensors")
+        dev = t.device
+    return dev
+
+
+def _f32(*ts):
+    for t in ts:
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("parameters and states must be float32")
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ attention
+def swa_meta_attn(q, k, v, n_meta: int, window: int, rope_base: float = 10000.0,
+                  pos0: int = 0, scale: float = 0.0, out=None, workspace=None):
+    """O = attention over X~ (meta prefix + causal sliding window), GQA, RoPE."""
+    dev = _dev(q, k, v, out)
+    B, T, Hq, Dh = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, T, Hkv, Dh) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k, v must be [B, T, Hkv, Dh] with q's dtype")
+    dt = dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    nb = lib.hm_swa_meta_attn_workspace(B, T, Hkv, Dh, dt)
+    ws = workspace if workspace is not None else _ws(nb, dev)
+    _check(lib.hm_swa_meta_attn(_p(q), _p(k), _p(v), _p(out), B, T, Hq, Hkv, Dh, n_meta, window,
+                                rope_base, pos0, scale, dt, _p(ws), ws.numel(), _stream()))
+    return out
+
+
+# ------------------------------------------------------------------ SSM branch
+def causal_conv1d(x, w, bias=None, state_in=None, apply_silu=True, state_out=None, out=None):
+    dev = _dev(x, w, bias, state_in, state_out, out)
+    _f32(w, bias, state_in, state_out)
+    B, T, Di = x.shape
+    K = w.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib.hm_causal_conv1d(_p(x), _p(w), _p(bias), _p(state_in), _p(out), _p(state_out), B, T,
+                                Di, K, int(bool(apply_silu)), dtype_code(x), _stream()))
+    return out
+
+
+def selective_scan(x, delta, A, Bm, Cm, D=None, z=None, h0=None, h_out=None, out=None,
+                   workspace=None):
+    dev = _dev(x, delta, A, Bm, Cm, D, z, h0, h_out, out)
+    _f32(A, D, h0, h_out)
+    B, T, Di = x.shape
+    N = A.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    nb = lib.hm_selective_scan_workspace(B, T, Di, N)
+    ws = workspace if workspace is not None else _ws(nb, dev)
+    _check(lib.hm_selective_scan(_p(x), _p(delta), _p(A), _p(Bm), _p(Cm), _p(D), _p(z), _p(h0),
+                                 _p(out), _p(h_out), B, T, Di, N, dtype_code(x), _p(ws),
+                                 ws.numel(), _stream()))
+    return out
+
+
+def conv_selective_scan(x, conv_w, conv_b, delta, A, Bm, Cm, D=None, z=None, conv_state_in=None,
+                        conv_state_out=None, h0=None, h_out=None, out=None, workspace=None):
+    dev = _dev(x, conv_w, conv_b, delta, A, Bm, Cm, D, z, conv_state_in, conv_state_out, h0,
+               h_out, out)
+    _f32(conv_w, conv_b, A, D, conv_state_in, conv_state_out, h0, h_out)
+    B, T, Di = x.shape
+    N, K = A.shape[1], conv_w.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    nb = lib.hm_selective_scan_workspace(B, T, Di, N)
+    ws = workspace if workspace is not None else _ws(nb, dev)
+    _check(lib.hm_conv_selective_scan(_p(x), _p(conv_w), _p(conv_b), _p(conv_state_in),
+                                      _p(conv_state_out), _p(delta), _p(A), _p(Bm), _p(Cm), _p(D),
+                                      _p(z), _p(h0), _p(out), _p(h_out), B, T, Di, K, N,
+                                      dtype_code(x), _p(ws), ws.numel(), _stream()))
+    return out
+
+
+# ------------------------------------------------------------------ fusion
+def branch_norm_mean(ya, ys, beta_a, beta_s, eps: float = 1e-6, out=None):
+    _dev(ya, ys, beta_a, beta_s, out)
+    _f32(beta_a, beta_s)
+    width = ya.shape[-1]
+    rows = ya.numel() // width
+    if out is None:
+        out = torch.empty_like(ya)
+    _check(lib.hm_branch_norm_mean(_p(ya), _p(ys), _p(beta_a), _p(beta_s), eps, _p(out), rows,
+                                   width, dtype_code(ya), _stream()))
+    return out
+
+
+# ------------------------------------------------------------------ whole layer
+class PrefillPlan:
+    """One prefill mixer layer with its outputs and workspace allocated once.
+
+    ``t`` maps the input names (q, k, v, x, delta, Bm, Cm, z, A, D, conv_w,
+    conv_b, beta_a, beta_s) to device tensors.  ``run()`` launches the layer on
+    the current stream and allocates nothing.
+    """
+
+    def __init__(self, t: dict, n_meta: int, window: int, rope_base: float = 10000.0,
+                 eps: float = 1e-6, pos0: int = 0, scale: float = 0.0, want_states=True,
+                 out=None, ya=None, ys=None, workspace=None):
+        q = t["q"]
+        dev = _dev(*[t[k] for k in ("q", "k", "v", "x", "delta", "Bm", "Cm", "z", "A", "D",
+                                     "conv_w", "conv_b", "beta_a", "beta_s")])
+        _f32(t["A"], t["D"], t["conv_w"], t["conv_b"], t["beta_a"], t["beta_s"])
+        B, T, Hq, Dh = q.shape
+        Di = t["x"].shape[2]
+        self.t = t
+        self.ya = ya if ya is not None else torch.empty((B, T, Di), dtype=q.dtype, device=dev)
+        self.ys = ys if ys is not None else torch.empty((B, T, Di), dtype=q.dtype, device=dev)
+        self.out = out if out is not None else torch.empty((B, T, Di), dtype=q.dtype, device=dev)
+        self.conv_state = self.h = None
+        if want_states:
+            self.conv_state = torch.empty((B, Di, t["conv_w"].shape[1] - 1), dtype=torch.float32,
+                                          device=dev)
+            self.h = torch.empty((B, Di, t["A"].shape[1]), dtype=torch.float32, device=dev)
+        a = PrefillArgs()
+        a.B, a.T, a.Hq, a.Hkv, a.Dh, a.Di = B, T, Hq, t["k"].shape[2], Dh, Di
+        a.N, a.K, a.n_meta, a.window = t["A"].shape[1], t["conv_w"].shape[1], n_meta, window
+        a.pos0, a.rope_base, a.scale, a.eps, a.dtype = pos0, rope_base, scale, eps, dtype_code(q)
+        for k in ("q", "k", "v", "x", "delta", "Bm", "Cm", "z", "A", "D", "conv_w", "conv_b",
+                  "beta_a", "beta_s"):
+            setattr(a, k, t[k].data_ptr())
+        a.ya, a.ys, a.out = self.ya.data_ptr(), self.ys.data_ptr(), self.out.data_ptr()
+        a.conv_state_out = self.conv_state.data_ptr() if want_states else None
+        a.h_out = self.h.data_ptr() if want_states else None
+        nb = lib.hm_mixer_prefill_workspace(ctypes.byref(a))
+        self.ws = workspace if workspace is not None else _ws(nb, dev)
+        a.workspace, a.workspace_bytes = self.ws.data_ptr(), self.ws.numel()
+        self.args = a
+
+    def run(self, stream=None):
+        s = _stream() if stream is None else ctypes.c_void_p(stream.cuda_stream)
+        _check(lib.hm_mixer_prefill(ctypes.byref(self.args), s))
+        return self.out
+
+
+def mixer_prefill(t: dict, n_meta: int, window: int, **kw):
+    plan = PrefillPlan(t, n_meta, window, **kw)
+    plan.run()
+    return {"ya": plan.ya, "ys": plan.ys, "out": plan.out, "conv_state": plan.conv_state,
+            "ssm_state": plan.h}
+
+
+class StepPlan:
+    """One decode token through one layer of a KV-sharing pair (see hm_mixer_step).
+
+    ``layer`` maps q, [k_new, v_new], x, delta, Bm, Cm, z, conv_state, ssm_state,
+    A, D, conv_w, conv_b, beta_a, beta_s to device tensors; conv_state and
+    ssm_state advance in place; the producer writes into k_cache / v_cache.
+    """
+
+    def __init__(self, layer: dict, k_cache, v_cache, n_prev: int, n_meta: int, window: int,
+                 rope_base: float = 10000.0, eps: float = 1e-6, scale: float = 0.0,
+                 want_branches=False, out=None, workspace=None):
+        q = layer["q"]
+        producer = layer.get("k_new") is not None
+        dev = _dev(q, k_cache, v_cache, layer.get("k_new"), layer.get("v_new"),
+                   *[layer[k] for k in ("x", "delta", "Bm", "Cm", "z", "conv_state", "ssm_state",
+                                        "A", "D", "conv_w", "conv_b", "beta_a", "beta_s")])
+        _f32(layer["conv_state"], layer["ssm_state"], layer["A"], layer["D"], layer["conv_w"],
+             layer["conv_b"], layer["beta_a"], layer["beta_s"])
+        B, Hq, Dh = q.shape
+        Di = layer["x"].shape[1]
+        a = StepArgs()
+        a.B, a.Hq, a.Hkv, a.Dh, a.Di = B, Hq, k_cache.shape[2], Dh, Di
+        a.N, a.K, a.n_meta, a.window = layer["A"].shape[1], layer["conv_w"].shape[1], n_meta, window
+        a.cache_slots = k_cache.shape[1] - n_meta
+        a.n_prev, a.rope_base, a.scale, a.eps, a.dtype = n_prev, rope_base, scale, eps, dtype_code(q)
+        a.q = q.data_ptr()
+        a.k_new = layer["k_new"].data_ptr() if producer else None
+        a.v_new = layer["v_new"].data_ptr() if producer else None
+        a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+        for k in ("x", "delta", "Bm", "Cm", "z", "A", "D", "conv_w", "conv_b", "conv_state",
+                  "ssm_state", "beta_a", "beta_s"):
+            setattr(a, k, layer[k].data_ptr())
+        self.out = out if out is not None else torch.empty((B, Di), dtype=q.dtype, device=dev)
+        a.out = self.out.data_ptr()
+        self.ya = self.ys = None
+        if want_branches:
+            self.ya = torch.empty((B, Di), dtype=torch.float32, device=dev)
+            self.ys = torch.empty((B, Di), dtype=torch.float32, device=dev)
+            a.ya_out, a.ys_out = self.ya.data_ptr(), self.ys.data_ptr()
+        nb = lib.hm_mixer_step_workspace(ctypes.byref(a))
+        self.ws = workspace if workspace is not None else _ws(nb, dev)
+        a.workspace, a.workspace_bytes = self.ws.data_ptr(), self.ws.numel()
+        self.args = a
+        self._keep = (layer, k_cache, v_cache)
+
+    def run(self, stream=None):
+        s = _stream() if stream is None else ctypes.c_void_p(stream.cuda_stream)
+        _check(lib.hm_mixer_step(ctypes.byref(self.args), s))
+        return self.out
+
+
+def mixer_step(layer: dict, k_cache, v_cache, n_prev: int, n_meta: int, window: int, **kw):
+    plan = StepPlan(layer, k_cache, v_cache, n_prev, n_meta, window, **kw)
+    plan.run()
+    return plan
+
+
+# ------------------------------------------------------------------ index exports
+def debug_attn_mask(T: int, n_meta: int, window: int, device="cuda"):
+    out = torch.empty((T, T), dtype=torch.uint8, device=device)
+    _check(lib.hm_debug_attn_mask(T, n_meta, window, _p(out), _stream()))
+    return out
+
+
+def debug_tile_plan(T: int, n_meta: int, window: int, bm: int, bn: int, device="cuda"):
+    nq, nk = -(-T // bm), -(-T // bn)
+    out = torch.empty((nq, nk), dtype=torch.int32, device=device)
+    _check(lib.hm_debug_tile_plan(T, n_meta, window, bm, bn, _p(out), out.numel(), _stream()))
+    return out
+
+
+def debug_attn_tiles():
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    lib.hm_debug_attn_tiles(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    return a.value, b.value, c.value
+
+
+def debug_cache_slot(n_prev: int, n_meta: int, window: int) -> int:
+    return lib.hm_debug_cache_slot(n_prev, n_meta, window)

@@ -1,0 +1,94 @@
+// libhm host layer: status strings, thread-local error text, and the one-call
+// mixer-layer prefill that chains attention, the SSM branch and the fusion
+// (Hymba blog, "数学表示" §6: both head types run on the same X~, then their
+// normalised outputs are averaged).
+#include <string>
+
+#include "hm_common.h"
+
+namespace hm {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+hm_status fail(hm_status s, const std::string& msg) {
+  g_last_error = std::string(hm_status_string(s)) + ": " + msg;
+  return s;
+}
+
+hm_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(HM_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return HM_OK;
+}
+
+}  // namespace hm
+
+extern "C" {
+
+int hm_abi_version(void) { return HM_ABI_VERSION; }
+
+const char* hm_status_string(hm_status s) {
+  switch (s) {
+    case HM_OK: return "HM_OK";
+    case HM_ERR_INVALID: return "HM_ERR_INVALID";
+    case HM_ERR_UNSUPPORTED: return "HM_ERR_UNSUPPORTED";
+    case HM_ERR_WORKSPACE: return "HM_ERR_WORKSPACE";
+    case HM_ERR_HIP: return "HM_ERR_HIP";
+  }
+  return "HM_ERR_UNKNOWN";
+}
+
+const char* hm_last_error(void) { return hm::g_last_error.c_str(); }
+
+// Workspace of one prefill layer: the attention scratch followed by the scan
+// scratch (each 256-byte aligned).
+size_t hm_mixer_prefill_workspace(const hm_prefill_args* a) {
+  if (!a) return 0;
+  size_t wa = hm_swa_meta_attn_workspace(a->B, a->T, a->Hkv, a->Dh, a->dtype);
+  size_t ws = hm_selective_scan_workspace(a->B, a->T, a->Di, a->N);
+  return hm::align_up(wa, 256) + hm::align_up(ws, 256);
+}
+
+hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream) {
+  HM_REQUIRE(a != nullptr, HM_ERR_INVALID, "args is NULL");
+  HM_REQUIRE(a->Di == a->Hq * a->Dh, HM_ERR_INVALID, "Di must equal Hq * Dh");
+  HM_PTR(a->ya);
+  HM_PTR(a->ys);
+  HM_PTR(a->out);
+  HM_REQUIRE(a->ya != a->ys && a->ya != a->out && a->ys != a->out, HM_ERR_INVALID,
+             "ya, ys and out must be distinct buffers");
+  size_t need = hm_mixer_prefill_workspace(a);
+  HM_REQUIRE(a->workspace != nullptr && a->workspace_bytes >= need, HM_ERR_WORKSPACE,
+             "workspace smaller than hm_mixer_prefill_workspace()");
+  size_t wa = hm::align_up(hm_swa_meta_attn_workspace(a->B, a->T, a->Hkv, a->Dh, a->dtype), 256);
+  char* ws = (char*)a->workspace;
+  hipStream_t st = (hipStream_t)stream;
+  // Validate all three parts before the first launch, so that a failure
+  // leaves every output untouched.
+  for (int pass = 0; pass < 2; ++pass) {
+    bool dry = pass == 0;
+    hm_status s = hm::swa_meta_attn_impl(a->q, a->k, a->v, a->ya, a->B, a->T, a->Hq, a->Hkv,
+                                         a->Dh, a->n_meta, a->window, a->rope_base, a->pos0,
+                                         a->scale, a->dtype, ws, wa, st, dry);
+    if (s != HM_OK) return s;
+    s = hm::conv_scan_impl(a->x, a->conv_w, a->conv_b, nullptr, a->conv_state_out, a->delta,
+                           a->A, a->Bm, a->Cm, a->D, a->z, nullptr, a->ys, a->h_out, a->B,
+                           a->T, a->Di, a->K, a->N, a->dtype, ws + wa, a->workspace_bytes - wa,
+                           st, /*fuse_conv=*/true, dry);
+    if (s != HM_OK) return s;
+    s = hm::norm_mean_impl(a->ya, a->ys, a->beta_a, a->beta_s, a->eps, a->out,
+                           (long long)a->B * a->T, a->Di, a->dtype, st, dry);
+    if (s != HM_OK) return s;
+  }
+  return HM_OK;
+}
+
+long long hm_debug_cache_slot(long long n_prev, int n_meta, int window) {
+  if (n_prev < 0) return -1;
+  return (long long)n_meta + (window > 0 ? n_prev % window : n_prev);
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// Branch normalisation and average of the hybrid-head mixer (Hymba blog,
+// juejin.cn "NVIDIA提出Hymba网络": "深入理解混合头模块" — both branches are
+// normalised to one scale and averaged; "数学表示" §5 — learnable rescale
+// vectors beta_1, beta_2):
+//   out = 0.5 * (beta_a * ya / rms(ya) + beta_s * ys / rms(ys)),
+//   rms(y) = sqrt(mean(y^2) + eps) over the whole branch width of a token.
+// One wave per row: a first pass accumulates both sums of squares in float32
+// (16-byte loads), a wave reduction, then a second pass over the row (served
+// from L1/L2) writes the output.  HBM traffic: read ya and ys once, write out.
+#include <cmath>
+
+#include "hm_common.h"
+
+namespace {
+
+HM_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+template <typename Tact>
+struct Vec8;
+template <>
+struct Vec8<bf16_t> {  // 8 bf16 = 16 bytes
+  static HM_DEV void ld(const bf16_t* p, float* f) {
+    uint4 r = *(const uint4*)p;
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  static HM_DEV void st(bf16_t* p, const float* f) {
+    uint4 r;
+    r.x = pack_bf16x2(f[0], f[1]);
+    r.y = pack_bf16x2(f[2], f[3]);
+    r.z = pack_bf16x2(f[4], f[5]);
+    r.w = pack_bf16x2(f[6], f[7]);
+    *(uint4*)p = r;
+  }
+};
+template <>
+struct Vec8<float> {  // 8 floats = two 16-byte accesses
+  static HM_DEV void ld(const float* p, float* f) {
+    float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+    f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+  static HM_DEV void st(float* p, const float* f) {
+    *(float4*)p = make_float4(f[0], f[1], f[2], f[3]);
+    *(float4*)(p + 4) = make_float4(f[4], f[5], f[6], f[7]);
+  }
+};
+
+// width % 8 == 0 (16-byte aligned rows)
+template <typename Tact>
+__global__ __launch_bounds__(256) void norm_mean_vec(const Tact* __restrict__ ya,
+                                                     const Tact* __restrict__ ys,
+                                                     const float* __restrict__ ba,
+                                                     const float* __restrict__ bs, float eps,
+                                                     Tact* __restrict__ out, long long rows,
+                                                     int width) {
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const Tact* pa = ya + row * width;
+  const Tact* ps = ys + row * width;
+  const int n8 = width >> 3;
+  float sa = 0.f, ss = 0.f;
+  for (int c = lane; c < n8; c += 64) {
+    float a[8], s[8];
+    Vec8<Tact>::ld(pa + 8 * c, a);
+    Vec8<Tact>::ld(ps + 8 * c, s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sa += a[i] * a[i];
+      ss += s[i] * s[i];
+    }
+  }
+  sa = wave_sum(sa);
+  ss = wave_sum(ss);
+  const float ra = 0.5f / sqrtf(sa / (float)width + eps);
+  const float rs = 0.5f / sqrtf(ss / (float)width + eps);
+  Tact* po = out + row * width;
+  for (int c = lane; c < n8; c += 64) {
+    float a[8], s[8], r[8];
+    Vec8<Tact>::ld(pa + 8 * c, a);
+    Vec8<Tact>::ld(ps + 8 * c, s);
+    const float4 ba0 = *(const float4*)(ba + 8 * c), ba1 = *(const float4*)(ba + 8 * c + 4);
+    const float4 bs0 = *(const float4*)(bs + 8 * c), bs1 = *(const float4*)(bs + 8 * c + 4);
+    const float wa[8] = {ba0.x, ba0.y, ba0.z, ba0.w, ba1.x, ba1.y, ba1.z, ba1.w};
+    const float wsv[8] = {bs0.x, bs0.y, bs0.z, bs0.w, bs1.x, bs1.y, bs1.z, bs1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = wa[i] * a[i] * ra + wsv[i] * s[i] * rs;
+    Vec8<Tact>::st(po + 8 * c, r);
+  }
+}
+
+// any width
+template <typename Tact>
+__global__ __launch_bounds__(256) void norm_mean_scalar(const Tact* __restrict__ ya,
+                                                        const Tact* __restrict__ ys,
+                                                        const float* __restrict__ ba,
+                                                        const float* __restrict__ bs, float eps,
+                                                        Tact* __restrict__ out, long long rows,
+                                                        int width) {
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const Tact* pa = ya + row * width;
+  const Tact* ps = ys + row * width;
+  float sa = 0.f, ss = 0.f;
+  for (int c = lane; c < width; c += 64) {
+    const float a = ActIO<Tact>::ld(pa + c), s = ActIO<Tact>::ld(ps + c);
+    sa += a * a;
+    ss += s * s;
+  }
+  sa = wave_sum(sa);
+  ss = wave_sum(ss);
+  const float ra = 0.5f / sqrtf(sa / (float)width + eps);
+  const float rs = 0.5f / sqrtf(ss / (float)width + eps);
+  Tact* po = out + row * width;
+  for (int c = lane; c < width; c += 64)
+    ActIO<Tact>::st(po + c, ba[c] * ActIO<Tact>::ld(pa + c) * ra + bs[c] * ActIO<Tact>::ld(ps + c) * rs);
+}
+
+template <typename Tact>
+void launch_norm(const void* ya, const void* ys, const float* ba, const float* bs, float eps,
+                 void* out, long long rows, int width, hipStream_t st) {
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (width % 8 == 0)
+    hipLaunchKernelGGL(norm_mean_vec<Tact>, grid, dim3(256), 0, st, (const Tact*)ya,
+                       (const Tact*)ys, ba, bs, eps, (Tact*)out, rows, width);
+  else
+    hipLaunchKernelGGL(norm_mean_scalar<Tact>, grid, dim3(256), 0, st, (const Tact*)ya,
+                       (const Tact*)ys, ba, bs, eps, (Tact*)out, rows, width);
+}
+
+}  // namespace
+
+namespace hm {
+
+hm_status norm_mean_impl(const void* ya, const void* ys, const float* beta_a,
+                         const float* beta_s, float eps, void* out, long long rows, int width,
+                         hm_dtype dtype, hipStream_t st, bool dry) {
+  HM_PTR(ya);
+  HM_PTR(ys);
+  HM_PTR(beta_a);
+  HM_PTR(beta_s);
+  HM_PTR(out);
+  HM_REQUIRE(rows > 0 && width > 0, HM_ERR_INVALID, "rows and width must be positive");
+  HM_REQUIRE(eps >= 0.f && std::isfinite(eps), HM_ERR_INVALID, "eps must be finite and >= 0");
+  HM_REQUIRE(dtype == HM_BF16 || dtype == HM_F32, HM_ERR_UNSUPPORTED, "dtype must be f32 or bf16");
+  HM_REQUIRE(out != ya && out != ys, HM_ERR_INVALID, "out must not alias ya or ys");
+  HM_REQUIRE((rows + 3) / 4 < (1LL << 31), HM_ERR_UNSUPPORTED, "too many rows");
+  if (dry) return HM_OK;
+  if (dtype == HM_BF16)
+    launch_norm<bf16_t>(ya, ys, beta_a, beta_s, eps, out, rows, width, st);
+  else
+    launch_norm<float>(ya, ys, beta_a, beta_s, eps, out, rows, width, st);
+  return check_launch("norm_mean");
+}
+
+}  // namespace hm
+
+extern "C" hm_status hm_branch_norm_mean(const void* ya, const void* ys, const float* beta_a,
+                                         const float* beta_s, float eps, void* out,
+                                         long long rows, int width, hm_dtype dtype,
+                                         void* stream) {
+  return hm::norm_mean_impl(ya, ys, beta_a, beta_s, eps, out, rows, width, dtype,
+                            (hipStream_t)stream, false);
+}

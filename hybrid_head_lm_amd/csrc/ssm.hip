@@ -1,0 +1,380 @@
+// SSM heads of the hybrid-head mixer: causal depthwise conv1d (width 4) and
+// the selective scan of Hymba blog (juejin.cn, "NVIDIA提出Hymba网络"),
+// "数学表示" §4, Eq. (2), in its recurrent form
+//     h_t = exp(delta_t A) h_{t-1} + (delta_t x_t) B_t,   y_t = C_t . h_t,
+// with the skip D x_t and the gate SiLU(z_t); 16 states per channel
+// (Hymba-1.5B-Base model card, "模型架构").
+//
+// Layout: x, delta, z, y are [B, T, Di] (channel fastest); B_t, C_t [B, T, 16]
+// are shared by every channel of a token.  One lane owns one channel and keeps
+// its 16 states in registers, so the state update needs no cross-lane work;
+// B_t and C_t are the same for the whole wave (scalar loads).  exp(delta A) is
+// computed as exp2(delta * A log2(e)).
+//
+// The time axis is cut into chunks so that B * ceil(Di/64) * chunks waves fill
+// the chip.  Three kernels:
+//   scan_chunk_agg   per chunk but the last: end state from a zero start, and
+//                    the chunk's total delta (its decay is exp(A * sum delta));
+//   scan_carry       per (b, state, channel): walks the chunks in order and
+//                    replaces each chunk's aggregate by its incoming state;
+//   scan_chunk_final per chunk: the recurrence from the incoming state, writing
+//                    y (and the final states for the last chunk).
+// With the fused conv the short convolution is recomputed from x (3-token halo)
+// inside both chunk kernels and never goes to memory.
+#include "hm_common.h"
+
+namespace {
+
+constexpr int kNS = 16;
+constexpr int kConvK = 4;
+constexpr int kMinChunk = 32;
+constexpr int kTargetWaves = 4096;
+
+HM_HD int scan_chunk_len(int B, int T, int Di) {
+  const int groups = B * ((Di + 63) / 64);
+  int nc = (kTargetWaves + groups - 1) / groups;
+  const int maxc = (T + kMinChunk - 1) / kMinChunk;
+  if (nc > maxc) nc = maxc;
+  if (nc < 1) nc = 1;
+  int L = (T + nc - 1) / nc;
+  return L < 1 ? 1 : L;
+}
+
+template <typename Tact>
+HM_DEV float ldx(const Tact* p) { return ActIO<Tact>::ld(p); }
+
+// Conv input at time t (t may be negative: then the state or zero).
+template <typename Tact>
+HM_DEV float conv_in(const Tact* xrow0, long long t, int Di, const float* st_in_c) {
+  if (t >= 0) return ldx(xrow0 + t * Di);
+  return st_in_c ? st_in_c[kConvK - 1 + t] : 0.f;
+}
+
+// ---------------------------------------------------------------- standalone conv
+template <typename Tact>
+__global__ __launch_bounds__(256) void conv1d_kernel(const Tact* __restrict__ x,
+                                                     const float* __restrict__ w,
+                                                     const float* __restrict__ bias,
+                                                     const float* __restrict__ st_in,
+                                                     Tact* __restrict__ y,
+                                                     float* __restrict__ st_out, int T, int Di,
+                                                     int silu, int tchunk) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= Di) return;
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.y * tchunk, t1 = min(T, t0 + tchunk);
+  const float w0 = w[c * 4 + 0], w1 = w[c * 4 + 1], w2 = w[c * 4 + 2], w3 = w[c * 4 + 3];
+  const float bb = bias ? bias[c] : 0.f;
+  const Tact* xc = x + (size_t)b * T * Di + c;
+  const float* sin_c = st_in ? st_in + ((size_t)b * Di + c) * 3 : nullptr;
+  float h0 = conv_in(xc, (long long)t0 - 3, Di, sin_c);
+  float h1 = conv_in(xc, (long long)t0 - 2, Di, sin_c);
+  float h2 = conv_in(xc, (long long)t0 - 1, Di, sin_c);
+  Tact* yc = y + (size_t)b * T * Di + c;
+  for (int t = t0; t < t1; ++t) {
+    const float xt = ldx(xc + (size_t)t * Di);
+    float u = bb + w0 * h0 + w1 * h1 + w2 * h2 + w3 * xt;
+    if (silu) u = siluf_(u);
+    ActIO<Tact>::st(yc + (size_t)t * Di, u);
+    h0 = h1;
+    h1 = h2;
+    h2 = xt;
+  }
+  if (st_out && blockIdx.y == gridDim.y - 1) {
+    float* so = st_out + ((size_t)b * Di + c) * 3;
+    for (int e = 0; e < 3; ++e) so[e] = conv_in(xc, (long long)T - 3 + e, Di, sin_c);
+  }
+}
+
+// ---------------------------------------------------------------- chunk aggregate
+template <typename Tact, bool CONV>
+__global__ __launch_bounds__(64) void scan_chunk_agg(
+    const Tact* __restrict__ x, const Tact* __restrict__ dl, const float* __restrict__ A,
+    const Tact* __restrict__ Bm, const float* __restrict__ cw, const float* __restrict__ cb,
+    const float* __restrict__ cst_in, float* __restrict__ E, float* __restrict__ S, int T,
+    int Di, int L, int nC) {
+  const int lane = threadIdx.x;
+  const int c0 = blockIdx.x * 64 + lane;
+  const bool active = c0 < Di;
+  const int c = active ? c0 : Di - 1;
+  const int k = blockIdx.y, b = blockIdx.z;
+  const int t0 = k * L, t1 = min(T, t0 + L);
+  float a2[kNS], h[kNS];
+#pragma unroll
+  for (int nn = 0; nn < kNS; ++nn) {
+    a2[nn] = A[c * kNS + nn] * kLog2e;
+    h[nn] = 0.f;
+  }
+  const Tact* xc = x + (size_t)b * T * Di + c;
+  const Tact* dc = dl + (size_t)b * T * Di + c;
+  float w0 = 0, w1 = 0, w2 = 0, w3 = 0, bb = 0, p0 = 0, p1 = 0, p2 = 0;
+  if (CONV) {
+    w0 = cw[c * 4 + 0]; w1 = cw[c * 4 + 1]; w2 = cw[c * 4 + 2]; w3 = cw[c * 4 + 3];
+    bb = cb[c];
+    const float* sc = cst_in ? cst_in + ((size_t)b * Di + c) * 3 : nullptr;
+    p0 = conv_in(xc, (long long)t0 - 3, Di, sc);
+    p1 = conv_in(xc, (long long)t0 - 2, Di, sc);
+    p2 = conv_in(xc, (long long)t0 - 1, Di, sc);
+  }
+  float ssum = 0.f;
+  const Tact* Bt = Bm + ((size_t)b * T + t0) * kNS;
+  for (int t = t0; t < t1; ++t, Bt += kNS) {
+    float xv = ldx(xc + (size_t)t * Di);
+    const float dv = ldx(dc + (size_t)t * Di);
+    if (CONV) {
+      const float u = bb + w0 * p0 + w1 * p1 + w2 * p2 + w3 * xv;
+      p0 = p1; p1 = p2; p2 = xv;
+      xv = siluf_(u);
+    }
+    const float du = dv * xv;
+#pragma unroll
+    for (int nn = 0; nn < kNS; ++nn) h[nn] = fast_exp2(dv * a2[nn]) * h[nn] + du * ldx(Bt + nn);
+    ssum += dv;
+  }
+  if (active) {
+    float* e = E + ((size_t)b * nC + k) * kNS * Di + c;
+#pragma unroll
+    for (int nn = 0; nn < kNS; ++nn) e[(size_t)nn * Di] = h[nn];
+    S[((size_t)b * nC + k) * Di + c] = ssum;
+  }
+}
+
+// ---------------------------------------------------------------- carry across chunks
+__global__ __launch_bounds__(256) void scan_carry(const float* __restrict__ A,
+                                                  const float* __restrict__ h0,
+                                                  float* __restrict__ E,
+                                                  const float* __restrict__ S, int Bsz,
+                                                  int Di, int nC) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long long)Bsz * kNS * Di) return;
+  const int c = idx % Di;
+  const int nn = (idx / Di) % kNS;
+  const int b = idx / ((long long)Di * kNS);
+  float H = h0 ? h0[((size_t)b * Di + c) * kNS + nn] : 0.f;
+  const float a2 = A[c * kNS + nn] * kLog2e;
+  for (int k = 0; k + 1 < nC; ++k) {
+    float* e = E + (((size_t)b * nC + k) * kNS + nn) * Di + c;
+    const float agg = *e;
+    *e = H;
+    H = fast_exp2(a2 * S[((size_t)b * nC + k) * Di + c]) * H + agg;
+  }
+  E[(((size_t)b * nC + nC - 1) * kNS + nn) * Di + c] = H;
+}
+
+// ---------------------------------------------------------------- final pass
+template <typename Tact, bool CONV>
+__global__ __launch_bounds__(64) void scan_chunk_final(
+    const Tact* __restrict__ x, const Tact* __restrict__ dl, const float* __restrict__ A,
+    const Tact* __restrict__ Bm, const Tact* __restrict__ Cm, const float* __restrict__ D,
+    const Tact* __restrict__ z, const float* __restrict__ cw, const float* __restrict__ cb,
+    const float* __restrict__ cst_in, float* __restrict__ cst_out,
+    const float* __restrict__ Hin, Tact* __restrict__ y, float* __restrict__ h_out, int T,
+    int Di, int L, int nC) {
+  const int lane = threadIdx.x;
+  const int c0 = blockIdx.x * 64 + lane;
+  const bool active = c0 < Di;
+  const int c = active ? c0 : Di - 1;
+  const int k = blockIdx.y, b = blockIdx.z;
+  const int t0 = k * L, t1 = min(T, t0 + L);
+  float a2[kNS], h[kNS];
+  const float* hin = Hin + ((size_t)b * nC + k) * kNS * Di + c;
+#pragma unroll
+  for (int nn = 0; nn < kNS; ++nn) {
+    a2[nn] = A[c * kNS + nn] * kLog2e;
+    h[nn] = hin[(size_t)nn * Di];
+  }
+  const float Dc = D ? D[c] : 0.f;
+  const Tact* xc = x + (size_t)b * T * Di + c;
+  const Tact* dc = dl + (size_t)b * T * Di + c;
+  const Tact* zc = z ? z + (size_t)b * T * Di + c : nullptr;
+  Tact* yc = y + (size_t)b * T * Di + c;
+  const float* sc = (CONV && cst_in) ? cst_in + ((size_t)b * Di + c) * 3 : nullptr;
+  float w0 = 0, w1 = 0, w2 = 0, w3 = 0, bb = 0, p0 = 0, p1 = 0, p2 = 0;
+  if (CONV) {
+    w0 = cw[c * 4 + 0]; w1 = cw[c * 4 + 1]; w2 = cw[c * 4 + 2]; w3 = cw[c * 4 + 3];
+    bb = cb[c];
+    p0 = conv_in(xc, (long long)t0 - 3, Di, sc);
+    p1 = conv_in(xc, (long long)t0 - 2, Di, sc);
+    p2 = conv_in(xc, (long long)t0 - 1, Di, sc);
+  }
+  const Tact* Bt = Bm + ((size_t)b * T + t0) * kNS;
+  const Tact* Ct = Cm + ((size_t)b * T + t0) * kNS;
+  for (int t = t0; t < t1; ++t, Bt += kNS, Ct += kNS) {
+    float xv = ldx(xc + (size_t)t * Di);
+    const float dv = ldx(dc + (size_t)t * Di);
+    if (CONV) {
+      const float u = bb + w0 * p0 + w1 * p1 + w2 * p2 + w3 * xv;
+      p0 = p1; p1 = p2; p2 = xv;
+      xv = siluf_(u);
+    }
+    const float du = dv * xv;
+    float yv = 0.f;
+#pragma unroll
+    for (int nn = 0; nn < kNS; ++nn) {
+      h[nn] = fast_exp2(dv * a2[nn]) * h[nn] + du * ldx(Bt + nn);
+      yv += ldx(Ct + nn) * h[nn];
+    }
+    yv += Dc * xv;
+    if (zc) yv *= siluf_(ldx(zc + (size_t)t * Di));
+    if (active) ActIO<Tact>::st(yc + (size_t)t * Di, yv);
+  }
+  if (k == nC - 1 && active) {
+    if (h_out) {
+      float* ho = h_out + ((size_t)b * Di + c) * kNS;
+#pragma unroll
+      for (int nn = 0; nn < kNS; ++nn) ho[nn] = h[nn];
+    }
+    if (CONV && cst_out) {
+      float* so = cst_out + ((size_t)b * Di + c) * 3;
+      for (int e = 0; e < 3; ++e) so[e] = conv_in(xc, (long long)T - 3 + e, Di, sc);
+    }
+  }
+}
+
+template <typename Tact, bool CONV>
+hm_status launch_scan(const void* x, const float* cw, const float* cb, const float* cst_in,
+                      float* cst_out, const void* delta, const float* A, const void* Bm,
+                      const void* Cm, const float* D, const void* z, const float* h0, void* y,
+                      float* h_out, int B, int T, int Di, void* workspace, hipStream_t st) {
+  const int L = scan_chunk_len(B, T, Di);
+  const int nC = (T + L - 1) / L;
+  float* E = (float*)workspace;
+  float* S = E + (size_t)B * nC * kNS * Di;
+  const dim3 blk(64);
+  const int gx = (Di + 63) / 64;
+  if (nC > 1) {
+    hipLaunchKernelGGL((scan_chunk_agg<Tact, CONV>), dim3(gx, nC - 1, B), blk, 0, st,
+                       (const Tact*)x, (const Tact*)delta, A, (const Tact*)Bm, cw, cb, cst_in, E,
+                       S, T, Di, L, nC);
+    hm_status s = hm::check_launch("scan_chunk_agg");
+    if (s != HM_OK) return s;
+  }
+  const long long nl = (long long)B * kNS * Di;
+  hipLaunchKernelGGL(scan_carry, dim3((unsigned)((nl + 255) / 256)), dim3(256), 0, st, A, h0, E,
+                     (const float*)S, B, Di, nC);
+  hm_status s = hm::check_launch("scan_carry");
+  if (s != HM_OK) return s;
+  hipLaunchKernelGGL((scan_chunk_final<Tact, CONV>), dim3(gx, nC, B), blk, 0, st,
+                     (const Tact*)x, (const Tact*)delta, A, (const Tact*)Bm, (const Tact*)Cm, D,
+                     (const Tact*)z, cw, cb, cst_in, cst_out, (const float*)E, (Tact*)y, h_out, T,
+                     Di, L, nC);
+  return hm::check_launch("scan_chunk_final");
+}
+
+}  // namespace
+
+namespace hm {
+
+hm_status conv_scan_impl(const void* x, const float* conv_w, const float* conv_b,
+                         const float* conv_state_in, float* conv_state_out,
+                         const void* delta, const float* A, const void* Bm, const void* Cm,
+                         const float* D, const void* z, const float* h0, void* y,
+                         float* h_out, int B, int T, int Di, int K, int N, hm_dtype dtype,
+                         void* workspace, size_t workspace_bytes, hipStream_t st,
+                         bool fuse_conv, bool dry) {
+  HM_PTR(x);
+  HM_PTR(delta);
+  HM_PTR(A);
+  HM_PTR(Bm);
+  HM_PTR(Cm);
+  HM_PTR(y);
+  HM_OPT_PTR(D);
+  HM_OPT_PTR(z);
+  HM_OPT_PTR(h0);
+  HM_OPT_PTR(h_out);
+  HM_REQUIRE(B > 0 && T > 0 && Di > 0, HM_ERR_INVALID, "B, T and Di must be positive");
+  HM_REQUIRE(N == kNS, HM_ERR_UNSUPPORTED, "only N = 16 states are supported");
+  HM_REQUIRE(dtype == HM_BF16 || dtype == HM_F32, HM_ERR_UNSUPPORTED, "dtype must be f32 or bf16");
+  HM_REQUIRE((double)B * T * Di < 4.0e9 && B <= 65535, HM_ERR_UNSUPPORTED, "tensor too large");
+  HM_REQUIRE(y != x && y != delta && y != z && y != Bm && y != Cm, HM_ERR_INVALID,
+             "y must not alias an input");
+  HM_REQUIRE(h_out == nullptr || h_out != h0, HM_ERR_INVALID, "h_out must not alias h0");
+  if (fuse_conv) {
+    HM_REQUIRE(K == kConvK, HM_ERR_UNSUPPORTED, "only conv width K = 4 is supported");
+    HM_PTR(conv_w);
+    HM_PTR(conv_b);
+    HM_OPT_PTR(conv_state_in);
+    HM_OPT_PTR(conv_state_out);
+    HM_REQUIRE(conv_state_out == nullptr || conv_state_out != conv_state_in, HM_ERR_INVALID,
+               "conv_state_out must not alias conv_state_in");
+  }
+  const size_t need = hm_selective_scan_workspace(B, T, Di, N);
+  HM_REQUIRE(workspace != nullptr && workspace_bytes >= need && aligned16(workspace),
+             HM_ERR_WORKSPACE, "workspace smaller than hm_selective_scan_workspace()");
+  if (dry) return HM_OK;
+  if (dtype == HM_BF16) {
+    if (fuse_conv)
+      return launch_scan<bf16_t, true>(x, conv_w, conv_b, conv_state_in, conv_state_out, delta,
+                                       A, Bm, Cm, D, z, h0, y, h_out, B, T, Di, workspace, st);
+    return launch_scan<bf16_t, false>(x, nullptr, nullptr, nullptr, nullptr, delta, A, Bm, Cm, D,
+                                      z, h0, y, h_out, B, T, Di, workspace, st);
+  }
+  if (fuse_conv)
+    return launch_scan<float, true>(x, conv_w, conv_b, conv_state_in, conv_state_out, delta, A,
+                                    Bm, Cm, D, z, h0, y, h_out, B, T, Di, workspace, st);
+  return launch_scan<float, false>(x, nullptr, nullptr, nullptr, nullptr, delta, A, Bm, Cm, D, z,
+                                   h0, y, h_out, B, T, Di, workspace, st);
+}
+
+}  // namespace hm
+
+extern "C" {
+
+size_t hm_selective_scan_workspace(int B, int T, int Di, int N) {
+  if (B <= 0 || T <= 0 || Di <= 0 || N != kNS) return 0;
+  const int L = scan_chunk_len(B, T, Di);
+  const size_t nC = (size_t)(T + L - 1) / L;
+  return (size_t)B * nC * (kNS + 1) * Di * sizeof(float);
+}
+
+hm_status hm_selective_scan(const void* x, const void* delta, const float* A, const void* Bm,
+                            const void* Cm, const float* D, const void* z, const float* h0,
+                            void* y, float* h_out, int B, int T, int Di, int N, hm_dtype dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return hm::conv_scan_impl(x, nullptr, nullptr, nullptr, nullptr, delta, A, Bm, Cm, D, z, h0,
+                            y, h_out, B, T, Di, kConvK, N, dtype, workspace, workspace_bytes,
+                            (hipStream_t)stream, false, false);
+}
+
+hm_status hm_conv_selective_scan(const void* x, const float* conv_w, const float* conv_b,
+                                 const float* conv_state_in, float* conv_state_out,
+                                 const void* delta, const float* A, const void* Bm,
+                                 const void* Cm, const float* D, const void* z, const float* h0,
+                                 void* y, float* h_out, int B, int T, int Di, int K, int N,
+                                 hm_dtype dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return hm::conv_scan_impl(x, conv_w, conv_b, conv_state_in, conv_state_out, delta, A, Bm, Cm,
+                            D, z, h0, y, h_out, B, T, Di, K, N, dtype, workspace, workspace_bytes,
+                            (hipStream_t)stream, true, false);
+}
+
+hm_status hm_causal_conv1d(const void* x, const float* w, const float* bias,
+                           const float* state_in, void* y, float* state_out, int B, int T,
+                           int Di, int K, int apply_silu, hm_dtype dtype, void* stream) {
+  HM_PTR(x);
+  HM_PTR(w);
+  HM_PTR(y);
+  HM_OPT_PTR(bias);
+  HM_OPT_PTR(state_in);
+  HM_OPT_PTR(state_out);
+  HM_REQUIRE(B > 0 && T > 0 && Di > 0, HM_ERR_INVALID, "B, T and Di must be positive");
+  HM_REQUIRE(K == kConvK, HM_ERR_UNSUPPORTED, "only conv width K = 4 is supported");
+  HM_REQUIRE(dtype == HM_BF16 || dtype == HM_F32, HM_ERR_UNSUPPORTED, "dtype must be f32 or bf16");
+  HM_REQUIRE(y != x, HM_ERR_INVALID, "y must not alias x");
+  HM_REQUIRE(state_out == nullptr || state_out != state_in, HM_ERR_INVALID,
+             "state_out must not alias state_in");
+  HM_REQUIRE((double)B * T * Di < 4.0e9 && B <= 65535 && T <= (1 << 22), HM_ERR_UNSUPPORTED,
+             "tensor too large");
+  const int tchunk = 64;
+  const dim3 grid((Di + 255) / 256, (T + tchunk - 1) / tchunk, B);
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == HM_BF16)
+    hipLaunchKernelGGL(conv1d_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)x, w, bias,
+                       state_in, (bf16_t*)y, state_out, T, Di, apply_silu, tchunk);
+  else
+    hipLaunchKernelGGL(conv1d_kernel<float>, grid, dim3(256), 0, st, (const float*)x, w, bias,
+                       state_in, (float*)y, state_out, T, Di, apply_silu, tchunk);
+  return hm::check_launch("conv1d_kernel");
+}
+
+}  // extern "C"

@@ -1,0 +1,517 @@
+// One decode token through one layer of an adjacent pair sharing a KV cache.
+//
+// Sources: adjacent sliding-window blocks share one KV cache (Hymba blog,
+// juejin.cn "NVIDIA提出Hymba网络", "Hymba 的整体架构"); generation with the
+// cache enabled (Hymba-1.5B-Base model card, "模型使用"); attention Eq. (1),
+// SSM Eq. (2) and the norm-and-average fusion ("数学表示" §3-§5).
+//
+// Cache rows per sequence: meta tokens 0..M-1, then a ring of window slots
+// (token s -> slot M + s mod W; global layers append).  K is stored rotated.
+// With one n_prev for the batch the visible rows are exactly the contiguous
+// range [0, M + min(n_prev+1, W)).
+//
+// Three launches per layer:
+//   step_ssm_kv      conv step + one scan step per (b, channel), in place on the
+//                    states, branch output to the workspace; the producer layer's
+//                    extra blocks rotate k_new and write k_new / v_new into the
+//                    token's slot (so the next launch sees them);
+//   step_attn_bf16   split over keys: a workgroup of 4 waves covers 256 cache
+//                    rows of one (b, kv group); each wave takes 64 rows, computes
+//                    S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (the group's query
+//                    heads on the 16 MFMA columns, K straight from HBM as the A
+//                    operand), a softmax, and O^T = V^T P^T with V^T staged
+//                    through LDS; the 4 waves merge in LDS and write one partial
+//                    (max, sum, unnormalised O) per head;
+//   step_combine     per sequence: merge the partials into Y_attn, then the
+//                    branch RMS norm, rescale and average with Y_ssm.
+// A float32 path (any Dh in {16, 32, 64}) replaces the split kernel with one
+// thread per (b, head) that writes a single partial.
+#include <cmath>
+
+#include "hm_common.h"
+
+namespace {
+
+constexpr int kNS = 16;
+constexpr int kKeysPerWG = 256;
+constexpr int kVRow = 72;  // padded LDS row of the transposed V tile (bf16 elements)
+
+template <typename Tact>
+HM_DEV float ldx(const Tact* p) { return ActIO<Tact>::ld(p); }
+
+// ---------------------------------------------------------------- SSM step + KV write
+template <typename Tact>
+__global__ __launch_bounds__(256) void step_ssm_kv(
+    const Tact* __restrict__ x, const Tact* __restrict__ dl, const Tact* __restrict__ Bm,
+    const Tact* __restrict__ Cm, const Tact* __restrict__ z, const float* __restrict__ A,
+    const float* __restrict__ D, const float* __restrict__ cw, const float* __restrict__ cb,
+    float* __restrict__ conv_state, float* __restrict__ ssm_state, float* __restrict__ ys_ws,
+    int B, int Di, int n_ssm_blocks, const Tact* __restrict__ k_new,
+    const Tact* __restrict__ v_new, Tact* __restrict__ k_cache, Tact* __restrict__ v_cache,
+    int Hkv, int Dh, int S, int slot, long long pos, double log2_base) {
+  if ((int)blockIdx.x < n_ssm_blocks) {
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)B * Di) return;
+    const int c = idx % Di;
+    const int b = idx / Di;
+    float* cs = conv_state + idx * 3;
+    const float s0 = cs[0], s1 = cs[1], s2 = cs[2];
+    const float xv = ldx(x + idx);
+    const float u = cb[c] + cw[c * 4 + 0] * s0 + cw[c * 4 + 1] * s1 + cw[c * 4 + 2] * s2 +
+                    cw[c * 4 + 3] * xv;
+    cs[0] = s1;
+    cs[1] = s2;
+    cs[2] = xv;
+    const float xc = siluf_(u);
+    const float dv = ldx(dl + idx);
+    const float du = dv * xc;
+    float* hs = ssm_state + idx * kNS;
+    const float4* h4 = (const float4*)hs;
+    float h[kNS];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 t = h4[i];
+      h[4 * i] = t.x; h[4 * i + 1] = t.y; h[4 * i + 2] = t.z; h[4 * i + 3] = t.w;
+    }
+    const Tact* Bb = Bm + (size_t)b * kNS;
+    const Tact* Cb = Cm + (size_t)b * kNS;
+    float yv = 0.f;
+#pragma unroll
+    for (int nn = 0; nn < kNS; ++nn) {
+      h[nn] = fast_exp2(dv * (A[c * kNS + nn] * kLog2e)) * h[nn] + du * ldx(Bb + nn);
+      yv += ldx(Cb + nn) * h[nn];
+    }
+    float4* o4 = (float4*)hs;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o4[i] = make_float4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
+    yv += D[c] * xc;
+    yv *= siluf_(ldx(z + idx));
+    ys_ws[idx] = yv;
+    return;
+  }
+  // producer: rotate k_new at pos and write k/v into the token's slot
+  const long long idx = (long long)(blockIdx.x - n_ssm_blocks) * 256 + threadIdx.x;
+  const int half = Dh / 2;
+  if (idx >= (long long)B * Hkv * half) return;
+  const int d = idx % half;
+  const int g = (idx / half) % Hkv;
+  const int b = idx / ((long long)half * Hkv);
+  const Tact* ks = k_new + ((size_t)b * Hkv + g) * Dh;
+  const Tact* vs = v_new + ((size_t)b * Hkv + g) * Dh;
+  float sn, cs;
+  rope_sincos(pos, d, Dh, log2_base, &sn, &cs);
+  const float x1 = ldx(ks + d), x2 = ldx(ks + d + half);
+  const size_t off = (((size_t)b * S + slot) * Hkv + g) * Dh;
+  ActIO<Tact>::st(k_cache + off + d, x1 * cs - x2 * sn);
+  ActIO<Tact>::st(k_cache + off + d + half, x2 * cs + x1 * sn);
+  v_cache[off + d] = vs[d];
+  v_cache[off + d + half] = vs[d + half];
+}
+
+// ---------------------------------------------------------------- bf16 split attention
+// part layout: [B*Hkv][n_split][grp][2 + 64]: max (log2 units), sum, O[64].
+__global__ __launch_bounds__(256) void step_attn_bf16(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+    float* __restrict__ part, int Hq, int Hkv, int S, int L, long long pos, float qscale,
+    double log2_base, int n_split) {
+  __shared__ __attribute__((aligned(16))) bf16_t sVt[4][64 * kVRow];
+  __shared__ float sm[4][16], sl[4][16];
+  __shared__ float sO[4][16][64];
+  const int split = blockIdx.x, pair = blockIdx.y;
+  const int b = pair / Hkv, g = pair % Hkv;
+  const int grp = Hq / Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, G = lane >> 4;
+
+  // Q^T fragment (B operand): lane holds head n of the group, dims 8G+e and 32+8G+e.
+  bf16x8_v qf[2];
+  if (n < grp) {
+    const bf16_t* src = q + ((size_t)b * Hq + g * grp + n) * 64;
+    const uint4 r0 = *(const uint4*)(src + 8 * G);
+    const uint4 r1 = *(const uint4*)(src + 32 + 8 * G);
+    const bf16_t* p0 = (const bf16_t*)&r0;
+    const bf16_t* p1 = (const bf16_t*)&r1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float sn, cs;
+      rope_sincos(pos, 8 * G + e, 64, log2_base, &sn, &cs);
+      const float x1 = bf2f(p0[e]), x2 = bf2f(p1[e]);
+      qf[0][e] = (__bf16)((x1 * cs - x2 * sn) * qscale);
+      qf[1][e] = (__bf16)((x2 * cs + x1 * sn) * qscale);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qf[0][e] = (__bf16)0.f;
+      qf[1][e] = (__bf16)0.f;
+    }
+  }
+
+  const int j0 = (split * 4 + wave) * 64;
+  float m_run = -1e30f, l_run = 0.f;
+  f32x4_v acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[db][i] = 0.f;
+
+  if (j0 < L) {
+    const size_t rs = (size_t)Hkv * 64;                   // cache row stride (elements)
+    const bf16_t* kbase = kc + ((size_t)b * S) * rs + (size_t)g * 64;
+    const bf16_t* vbase = vc + ((size_t)b * S) * rs + (size_t)g * 64;
+    // K rows in the order that gives each lane group 8 consecutive keys per
+    // 32-key step of the output.
+    bf16x8_v kf[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = j0 + 32 * (kb >> 1) + 8 * (n >> 2) + 4 * (kb & 1) + (n & 3);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (key < L) {
+          kf[kb][s] = *(const bf16x8_v*)(kbase + (size_t)key * rs + 32 * s + 8 * G);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kf[kb][s][e] = (__bf16)0.f;
+        }
+      }
+    }
+    // V tile -> LDS transposed: lane = key, 8 chunks of 8 dims.
+    {
+      const int key = j0 + lane;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        uint4 val = {0u, 0u, 0u, 0u};
+        if (key < L) val = *(const uint4*)(vbase + (size_t)key * rs + 8 * r);
+        const bf16_t* pv = (const bf16_t*)&val;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sVt[wave][(8 * r + e) * kVRow + lane] = pv[e];
+      }
+    }
+    f32x4_v sc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[kb][i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[s], sc[kb], 0, 0, 0);
+    }
+    const float NEG_INF = -__builtin_huge_valf();
+    float mx = NEG_INF;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = j0 + 32 * (kb >> 1) + 8 * G + 4 * (kb & 1) + i;
+        if (key >= L) sc[kb][i] = NEG_INF;
+        mx = fmaxf(mx, sc[kb][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    m_run = mx;
+    bf16x8_v pf[2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(sc[kb][i] - mx);
+        l_run += p;
+        pf[kb >> 1][4 * (kb & 1) + i] = (__bf16)p;
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8_v a = *(const bf16x8_v*)(&sVt[wave][(16 * db + n) * kVRow + 32 * s + 8 * G]);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[s], acc[db], 0, 0, 0);
+      }
+  }
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (G == 0) {
+    sm[wave][n] = m_run;
+    sl[wave][n] = l_run;
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sO[wave][n][16 * db + 4 * G + i] = acc[db][i];
+  __syncthreads();
+  float* dst = part + ((size_t)pair * n_split + split) * grp * 66;
+  for (int idx = threadIdx.x; idx < grp * 64; idx += 256) {
+    const int hh = idx >> 6, d = idx & 63;
+    float M = sm[0][hh];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm[w][hh]);
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = fast_exp2(sm[w][hh] - M);
+      Ls += sl[w][hh] * f;
+      O += sO[w][hh][d] * f;
+    }
+    float* ph = dst + hh * 66;
+    if (d == 0) {
+      ph[0] = M;
+      ph[1] = Ls;
+    }
+    ph[2 + d] = O;
+  }
+}
+
+// ---------------------------------------------------------------- float32 attention
+template <int DH>
+__global__ __launch_bounds__(64) void step_attn_f32(const float* __restrict__ q,
+                                                    const float* __restrict__ kc,
+                                                    const float* __restrict__ vc,
+                                                    float* __restrict__ part, int B, int Hq,
+                                                    int Hkv, int S, int L, long long pos,
+                                                    float qscale, double log2_base) {
+  const int idx = blockIdx.x * 64 + threadIdx.x;
+  if (idx >= B * Hq) return;
+  const int h = idx % Hq, b = idx / Hq;
+  const int grp = Hq / Hkv, g = h / grp;
+  float qr[DH];
+  const float* src = q + ((size_t)b * Hq + h) * DH;
+#pragma unroll
+  for (int d = 0; d < DH / 2; ++d) {
+    float sn, cs;
+    rope_sincos(pos, d, DH, log2_base, &sn, &cs);
+    const float x1 = src[d], x2 = src[d + DH / 2];
+    qr[d] = (x1 * cs - x2 * sn) * qscale;
+    qr[d + DH / 2] = (x2 * cs + x1 * sn) * qscale;
+  }
+  float acc[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) acc[d] = 0.f;
+  float m = -1e30f, l = 0.f;
+  for (int j = 0; j < L; ++j) {
+    const float* kr = kc + (((size_t)b * S + j) * Hkv + g) * DH;
+    const float* vr = vc + (((size_t)b * S + j) * Hkv + g) * DH;
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) s += qr[d] * kr[d];
+    const float mn = fmaxf(m, s);
+    const float alpha = exp2f(m - mn), p = exp2f(s - mn);
+    l = l * alpha + p;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) acc[d] = acc[d] * alpha + p * vr[d];
+    m = mn;
+  }
+  float* ph = part + ((size_t)(b * Hkv + g) * grp + (h % grp)) * (DH + 2);
+  ph[0] = m;
+  ph[1] = l;
+#pragma unroll
+  for (int d = 0; d < DH; ++d) ph[2 + d] = acc[d];
+}
+
+// ---------------------------------------------------------------- combine + fusion
+template <typename Tact>
+__global__ __launch_bounds__(256) void step_combine(
+    const float* __restrict__ part, const float* __restrict__ ys_ws,
+    const float* __restrict__ ba, const float* __restrict__ bs, float eps, Tact* __restrict__ out,
+    float* __restrict__ ya_out, float* __restrict__ ys_out, int Hq, int Hkv, int Dh,
+    int n_split, int Di) {
+  __shared__ float sya[4096];
+  __shared__ float red[2][4];
+  const int b = blockIdx.x;
+  const int grp = Hq / Hkv;
+  const int stride = Dh + 2;
+  float sa = 0.f, ss = 0.f;
+  for (int idx = threadIdx.x; idx < Di; idx += 256) {
+    const int h = idx / Dh, d = idx % Dh;
+    const int g = h / grp, hh = h % grp;
+    const float* base = part + ((size_t)(b * Hkv + g) * n_split) * grp * stride + hh * stride;
+    float M = base[0];
+    for (int s = 1; s < n_split; ++s) M = fmaxf(M, base[(size_t)s * grp * stride]);
+    float Ls = 0.f, O = 0.f;
+    for (int s = 0; s < n_split; ++s) {
+      const float* ps = base + (size_t)s * grp * stride;
+      const float f = fast_exp2(ps[0] - M);
+      Ls += ps[1] * f;
+      O += ps[2 + d] * f;
+    }
+    const float ya = O / Ls;
+    sya[idx] = ya;
+    sa += ya * ya;
+    const float yv = ys_ws[(size_t)b * Di + idx];
+    ss += yv * yv;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    sa += __shfl_xor(sa, off);
+    ss += __shfl_xor(ss, off);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = sa;
+    red[1][threadIdx.x >> 6] = ss;
+  }
+  __syncthreads();
+  sa = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  ss = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const float ra = 0.5f / sqrtf(sa / (float)Di + eps);
+  const float rs = 0.5f / sqrtf(ss / (float)Di + eps);
+  for (int idx = threadIdx.x; idx < Di; idx += 256) {
+    const float ya = sya[idx];
+    const float yv = ys_ws[(size_t)b * Di + idx];
+    ActIO<Tact>::st(out + (size_t)b * Di + idx, ba[idx] * ya * ra + bs[idx] * yv * rs);
+    if (ya_out) ya_out[(size_t)b * Di + idx] = ya;
+    if (ys_out) ys_out[(size_t)b * Di + idx] = yv;
+  }
+}
+
+struct StepGeom {
+  int L, n_split, grp;
+  size_t ys_bytes, part_bytes;
+};
+
+StepGeom step_geom(const hm_step_args* a) {
+  StepGeom s{};
+  const long long nv = a->window > 0 ? (a->n_prev + 1 < a->window ? a->n_prev + 1 : a->window)
+                                     : a->n_prev + 1;
+  s.L = (int)(a->n_meta + nv);
+  s.grp = a->Hkv > 0 ? a->Hq / a->Hkv : 0;
+  s.n_split = a->dtype == HM_BF16 ? (s.L + kKeysPerWG - 1) / kKeysPerWG : 1;
+  s.ys_bytes = hm::align_up((size_t)a->B * a->Di * sizeof(float), 256);
+  s.part_bytes = (size_t)a->B * a->Hkv * s.n_split * s.grp * (a->Dh + 2) * sizeof(float);
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hm_mixer_step_workspace(const hm_step_args* a) {
+  if (!a || a->B <= 0 || a->Hkv <= 0 || a->Hq <= 0 || a->Di <= 0 || a->Dh <= 0 || a->n_prev < 0)
+    return 0;
+  const StepGeom s = step_geom(a);
+  return s.ys_bytes + s.part_bytes;
+}
+
+hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
+  HM_REQUIRE(a != nullptr, HM_ERR_INVALID, "args is NULL");
+  HM_REQUIRE(a->B > 0 && a->Hq > 0 && a->Hkv > 0 && a->Dh > 0 && a->Di > 0, HM_ERR_INVALID,
+             "B, Hq, Hkv, Dh and Di must be positive");
+  HM_REQUIRE(a->Hq % a->Hkv == 0, HM_ERR_INVALID, "Hq must be a multiple of Hkv");
+  HM_REQUIRE(a->Di == a->Hq * a->Dh, HM_ERR_INVALID, "Di must equal Hq * Dh");
+  HM_REQUIRE(a->n_prev >= 0, HM_ERR_INVALID, "n_prev must be >= 0");
+  HM_REQUIRE(a->n_meta >= 0 && a->cache_slots > 0, HM_ERR_INVALID,
+             "n_meta >= 0 and cache_slots > 0 required");
+  if (a->window > 0)
+    HM_REQUIRE(a->cache_slots >= a->window, HM_ERR_INVALID, "cache_slots must be >= window");
+  else
+    HM_REQUIRE(a->n_prev < a->cache_slots, HM_ERR_INVALID,
+               "global layer: n_prev must be < cache_slots");
+  HM_REQUIRE(a->N == kNS, HM_ERR_UNSUPPORTED, "only N = 16 states are supported");
+  HM_REQUIRE(a->K == 4, HM_ERR_UNSUPPORTED, "only conv width K = 4 is supported");
+  HM_REQUIRE(a->dtype == HM_BF16 || a->dtype == HM_F32, HM_ERR_UNSUPPORTED,
+             "dtype must be f32 or bf16");
+  if (a->dtype == HM_BF16)
+    HM_REQUIRE(a->Dh == 64 && a->Hq / a->Hkv <= 16, HM_ERR_UNSUPPORTED,
+               "bf16 decode supports Dh = 64 and at most 16 query heads per KV head");
+  else
+    HM_REQUIRE(a->Dh == 16 || a->Dh == 32 || a->Dh == 64, HM_ERR_UNSUPPORTED,
+               "f32 decode supports Dh in {16, 32, 64}");
+  HM_REQUIRE(a->Di <= 4096, HM_ERR_UNSUPPORTED, "Di must be <= 4096");
+  HM_REQUIRE(a->rope_base > 1.0f && std::isfinite(a->rope_base) && std::isfinite(a->scale) &&
+                 a->eps >= 0.f && std::isfinite(a->eps),
+             HM_ERR_INVALID, "rope_base > 1, finite scale and eps >= 0 required");
+  HM_PTR(a->q);
+  HM_PTR(a->k_cache);
+  HM_PTR(a->v_cache);
+  HM_PTR(a->x);
+  HM_PTR(a->delta);
+  HM_PTR(a->Bm);
+  HM_PTR(a->Cm);
+  HM_PTR(a->z);
+  HM_PTR(a->A);
+  HM_PTR(a->D);
+  HM_PTR(a->conv_w);
+  HM_PTR(a->conv_b);
+  HM_PTR(a->conv_state);
+  HM_PTR(a->ssm_state);
+  HM_PTR(a->beta_a);
+  HM_PTR(a->beta_s);
+  HM_PTR(a->out);
+  HM_OPT_PTR(a->ya_out);
+  HM_OPT_PTR(a->ys_out);
+  const bool producer = a->k_new != nullptr;
+  HM_REQUIRE(producer == (a->v_new != nullptr), HM_ERR_INVALID,
+             "k_new and v_new must both be set (producer) or both NULL (consumer)");
+  if (producer) {
+    HM_PTR(a->k_new);
+    HM_PTR(a->v_new);
+  }
+  HM_REQUIRE((double)a->B * (a->n_meta + a->cache_slots) * a->Hkv * a->Dh < 4.0e9,
+             HM_ERR_UNSUPPORTED, "cache too large");
+  const StepGeom g = step_geom(a);
+  const size_t need = g.ys_bytes + g.part_bytes;
+  HM_REQUIRE(a->workspace != nullptr && a->workspace_bytes >= need && hm::aligned16(a->workspace),
+             HM_ERR_WORKSPACE, "workspace smaller than hm_mixer_step_workspace()");
+
+  hipStream_t st = (hipStream_t)stream;
+  float* ys_ws = (float*)a->workspace;
+  float* part = (float*)((char*)a->workspace + g.ys_bytes);
+  const int S = a->n_meta + a->cache_slots;
+  const long long pos = (long long)a->n_meta + a->n_prev;
+  const int slot = (int)hm_debug_cache_slot(a->n_prev, a->n_meta, a->window);
+  const double l2b = log2((double)a->rope_base);
+  const float sc = (a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)a->Dh)) * kLog2e;
+  const int n_ssm_blocks = (int)(((long long)a->B * a->Di + 255) / 256);
+  const int n_kv_blocks =
+      producer ? (int)(((long long)a->B * a->Hkv * (a->Dh / 2) + 255) / 256) : 0;
+
+  if (a->dtype == HM_BF16) {
+    hipLaunchKernelGGL(step_ssm_kv<bf16_t>, dim3(n_ssm_blocks + n_kv_blocks), dim3(256), 0, st,
+                       (const bf16_t*)a->x, (const bf16_t*)a->delta, (const bf16_t*)a->Bm,
+                       (const bf16_t*)a->Cm, (const bf16_t*)a->z, a->A, a->D, a->conv_w,
+                       a->conv_b, a->conv_state, a->ssm_state, ys_ws, a->B, a->Di, n_ssm_blocks,
+                       (const bf16_t*)a->k_new, (const bf16_t*)a->v_new, (bf16_t*)a->k_cache,
+                       (bf16_t*)a->v_cache, a->Hkv, a->Dh, S, slot, pos, l2b);
+    hm_status s = hm::check_launch("step_ssm_kv");
+    if (s != HM_OK) return s;
+    hipLaunchKernelGGL(step_attn_bf16, dim3(g.n_split, a->B * a->Hkv), dim3(256), 0, st,
+                       (const bf16_t*)a->q, (const bf16_t*)a->k_cache,
+                       (const bf16_t*)a->v_cache, part, a->Hq, a->Hkv, S, g.L, pos, sc, l2b,
+                       g.n_split);
+    s = hm::check_launch("step_attn_bf16");
+    if (s != HM_OK) return s;
+    hipLaunchKernelGGL(step_combine<bf16_t>, dim3(a->B), dim3(256), 0, st, (const float*)part,
+                       (const float*)ys_ws, a->beta_a, a->beta_s, a->eps, (bf16_t*)a->out,
+                       a->ya_out, a->ys_out, a->Hq, a->Hkv, a->Dh, g.n_split, a->Di);
+    return hm::check_launch("step_combine");
+  }
+  hipLaunchKernelGGL(step_ssm_kv<float>, dim3(n_ssm_blocks + n_kv_blocks), dim3(256), 0, st,
+                     (const float*)a->x, (const float*)a->delta, (const float*)a->Bm,
+                     (const float*)a->Cm, (const float*)a->z, a->A, a->D, a->conv_w, a->conv_b,
+                     a->conv_state, a->ssm_state, ys_ws, a->B, a->Di, n_ssm_blocks,
+                     (const float*)a->k_new, (const float*)a->v_new, (float*)a->k_cache,
+                     (float*)a->v_cache, a->Hkv, a->Dh, S, slot, pos, l2b);
+  hm_status s = hm::check_launch("step_ssm_kv");
+  if (s != HM_OK) return s;
+  const int nbh = (a->B * a->Hq + 63) / 64;
+#define HM_STEP_F32(DHV)                                                                      \
+  case DHV:                                                                                   \
+    hipLaunchKernelGGL(step_attn_f32<DHV>, dim3(nbh), dim3(64), 0, st, (const float*)a->q,   \
+                       (const float*)a->k_cache, (const float*)a->v_cache, part, a->B, a->Hq,  \
+                       a->Hkv, S, g.L, pos, sc, l2b);                                          \
+    break;
+  switch (a->Dh) {
+    HM_STEP_F32(16)
+    HM_STEP_F32(32)
+    HM_STEP_F32(64)
+  }
+#undef HM_STEP_F32
+  s = hm::check_launch("step_attn_f32");
+  if (s != HM_OK) return s;
+  hipLaunchKernelGGL(step_combine<float>, dim3(a->B), dim3(256), 0, st, (const float*)part,
+                     (const float*)ys_ws, a->beta_a, a->beta_s, a->eps, (float*)a->out, a->ya_out,
+                     a->ys_out, a->Hq, a->Hkv, a->Dh, 1, a->Di);
+  return hm::check_launch("step_combine");
+}
+
+}  // extern "C"

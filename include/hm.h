@@ -1,0 +1,228 @@
+/*
+ * hm.h — C ABI of the Hymba hybrid-head mixer core on AMD MI355X (gfx950).
+ *
+ * The mixer is the hybrid-head module of Hymba: attention heads and SSM heads
+ * read the same projected input X~ = [meta tokens; tokens] in parallel, each
+ * branch output is normalised and rescaled by a learnable vector, and the two
+ * are averaged.  Sources (web pages on Hymba):
+ *   - juejin.cn blog "NVIDIA提出Hymba网络，Mamba+Attenation解决transformer的长序列
+ *     低效难题" (below: Hymba blog): sections "深入理解混合头模块" (module),
+ *     "数学表示" §1 (X~ = [R, X]), §2 (input projection), §3 Eq. (1) (attention),
+ *     §4 Eq. (2) (SSM heads), §5 (norm, rescale, fuse), "Hymba 的整体架构"
+ *     (global first/middle/last layers, sliding window elsewhere, adjacent
+ *     layers share the KV cache);
+ *   - Hymba-1.5B-Base model card, "模型架构" (GQA, RoPE, 16 SSM states).
+ * The projections W_in_proj and W_out_proj are outside this library: every
+ * call takes already-projected tensors.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise; tensors are
+ *     row-major and contiguous (last index fastest) and 16-byte aligned.
+ *   - Activations (q, k, v, o, x, delta, B, C, z, y, caches, out) have the
+ *     dtype given by `dtype`; parameters (A, D, conv weights and bias, beta)
+ *     and recurrent states are float32.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the null stream).  The library never synchronises, never
+ *     allocates device memory and keeps no pointer after a call returns.  The
+ *     caller owns every buffer; outputs must not alias inputs except the
+ *     documented in/out states and caches.  Scratch memory is passed in as
+ *     `workspace`, sized by the matching *_workspace() query.
+ *   - Every argument is validated before anything is launched, so on failure
+ *     no output is touched.  Errors are returned as hm_status; nothing aborts
+ *     or throws across the ABI.  hm_last_error() gives a message for the last
+ *     failing call on the calling thread.
+ */
+#ifndef HM_H_
+#define HM_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HM_ABI_VERSION 1
+
+typedef enum {
+  HM_OK = 0,
+  HM_ERR_INVALID = 1,      /* NULL required pointer, bad size or alignment      */
+  HM_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head dim, states, ...) */
+  HM_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required        */
+  HM_ERR_HIP = 4           /* a HIP launch failed; see hm_last_error()          */
+} hm_status;
+
+typedef enum { HM_F32 = 0, HM_BF16 = 1 } hm_dtype;
+
+int hm_abi_version(void);                       /* == HM_ABI_VERSION */
+const char* hm_status_string(hm_status s);      /* static string, never NULL */
+const char* hm_last_error(void);                /* thread-local, "" if none */
+
+/* ------------------------------------------------------------------------
+ * Attention heads over X~ (Hymba blog, 数学表示 §3 Eq. (1); sliding window and
+ * always-visible meta tokens: Hymba简介 and Hymba 的整体架构; GQA and RoPE:
+ * model card 模型架构).
+ *
+ *   O[b,i,h,:] = sum_j softmax_j( scale * <rope(q[b,i,h]), rope(k[b,j,g])> ) v[b,j,g]
+ *   over the keys j visible from row i:  j <= i  and  (j < n_meta or
+ *   window <= 0 or i - j < window);  g = h / (Hq / Hkv).
+ *
+ * q, o: [B, T, Hq, Dh];  k, v: [B, T, Hkv, Dh] (k before RoPE).  Rows of X~
+ * are meta tokens 0..n_meta-1 followed by tokens; row i has position pos0+i.
+ * RoPE is the rotate-half form on pairs (d, d + Dh/2) with angle
+ * pos * rope_base^(-2d/Dh) (angles evaluated in double precision).
+ * scale <= 0 selects 1/sqrt(Dh).  window <= 0 selects global causal attention.
+ * Supported: bf16 with Dh = 64 (MFMA path, float32 accumulation and softmax);
+ * float32 with Dh in {16, 32, 64} (float32 path).
+ * Workspace: hm_swa_meta_attn_workspace() bytes (rotated K and transposed V).
+ * ---------------------------------------------------------------------- */
+hm_status hm_swa_meta_attn(const void* q, const void* k, const void* v, void* o,
+                           int B, int T, int Hq, int Hkv, int Dh, int n_meta,
+                           int window, float rope_base, long long pos0, float scale,
+                           hm_dtype dtype, void* workspace, size_t workspace_bytes,
+                           void* stream);
+size_t hm_swa_meta_attn_workspace(int B, int T, int Hkv, int Dh, hm_dtype dtype);
+
+/* ------------------------------------------------------------------------
+ * Causal depthwise conv1d in front of the scan (the short convolution of a
+ * Mamba head; not printed on the pages):
+ *   y[b,t,c] = act( bias[c] + sum_{k<K} w[c,k] * x[b, t-K+1+k, c] )
+ * act = SiLU if apply_silu else identity.  Inputs before t = 0 come from
+ * state_in[b, c, 0..K-2] (oldest first) or are zero when state_in is NULL.
+ * state_out (may be NULL) receives the last K-1 inputs (oldest first).
+ * x, y: [B, T, Di]; w: [Di, K] f32; bias: [Di] f32 or NULL;
+ * state_in/state_out: [B, Di, K-1] f32.  Supported: K = 4.
+ * ---------------------------------------------------------------------- */
+hm_status hm_causal_conv1d(const void* x, const float* w, const float* bias,
+                           const float* state_in, void* y, float* state_out,
+                           int B, int T, int Di, int K, int apply_silu,
+                           hm_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Selective scan of the SSM heads (Hymba blog, 数学表示 §4 Eq. (2), recurrent
+ * form), N states per channel:
+ *   h_t = exp(delta_t * A) * h_{t-1} + (delta_t * x_t) * B_t
+ *   y_t = (C_t . h_t + D * x_t) * SiLU(z_t)
+ * x, delta, z, y: [B, T, Di] (delta >= 0, already passed through softplus);
+ * Bm, Cm: [B, T, N]; A: [Di, N] f32; D: [Di] f32 or NULL (no skip);
+ * z NULL: no gate; h0: [B, Di, N] f32 or NULL (zero start);
+ * h_out: [B, Di, N] f32 or NULL.  Supported: N = 16.
+ * Workspace: hm_selective_scan_workspace() bytes (per-chunk carries).
+ * ---------------------------------------------------------------------- */
+hm_status hm_selective_scan(const void* x, const void* delta, const float* A,
+                            const void* Bm, const void* Cm, const float* D,
+                            const void* z, const float* h0, void* y, float* h_out,
+                            int B, int T, int Di, int N, hm_dtype dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+size_t hm_selective_scan_workspace(int B, int T, int Di, int N);
+
+/* Same as hm_causal_conv1d (SiLU) followed by hm_selective_scan on its output,
+ * in one pass over x (the conv output never goes to memory).  conv_state_in /
+ * conv_state_out as state_in / state_out above.  Same workspace as the scan. */
+hm_status hm_conv_selective_scan(const void* x, const float* conv_w,
+                                 const float* conv_b, const float* conv_state_in,
+                                 float* conv_state_out, const void* delta,
+                                 const float* A, const void* Bm, const void* Cm,
+                                 const float* D, const void* z, const float* h0,
+                                 void* y, float* h_out, int B, int T, int Di, int K,
+                                 int N, hm_dtype dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Branch normalisation and average (Hymba blog, 深入理解混合头模块 and
+ * 数学表示 §5):  per row r,
+ *   out[r,:] = 0.5 * ( beta_a * ya[r,:] / rms(ya[r,:]) + beta_s * ys[r,:] / rms(ys[r,:]) )
+ *   rms(y) = sqrt(mean(y^2) + eps)
+ * ya, ys, out: [rows, width]; beta_a, beta_s: [width] f32.
+ * ---------------------------------------------------------------------- */
+hm_status hm_branch_norm_mean(const void* ya, const void* ys, const float* beta_a,
+                              const float* beta_s, float eps, void* out,
+                              long long rows, int width, hm_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * One whole mixer layer in prefill: attention (hm_swa_meta_attn) and the SSM
+ * branch (hm_conv_selective_scan from zero states) on the same X~, then
+ * hm_branch_norm_mean.  Width Di must equal Hq * Dh.
+ * ya, ys: [B, T, Di] branch outputs (written; caller-owned, act dtype);
+ * out: [B, T, Di].  conv_state_out [B, Di, K-1] and h_out [B, Di, N] (f32,
+ * may be NULL) receive the final SSM-branch states for a following decode.
+ * Workspace: hm_mixer_prefill_workspace() bytes.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int B, T, Hq, Hkv, Dh, Di, N, K, n_meta, window;
+  long long pos0;
+  float rope_base, scale, eps;
+  hm_dtype dtype;
+  const void *q, *k, *v;                      /* [B,T,Hq,Dh], [B,T,Hkv,Dh] x2 */
+  const void *x, *delta, *Bm, *Cm, *z;        /* [B,T,Di] x2, [B,T,N] x2, [B,T,Di] */
+  const float *A, *D, *conv_w, *conv_b;       /* [Di,N], [Di], [Di,K], [Di] */
+  const float *beta_a, *beta_s;               /* [Di] */
+  void *ya, *ys, *out;                        /* [B,T,Di] each */
+  float *conv_state_out, *h_out;              /* optional */
+  void* workspace;
+  size_t workspace_bytes;
+} hm_prefill_args;
+hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream);
+size_t hm_mixer_prefill_workspace(const hm_prefill_args* a);
+
+/* ------------------------------------------------------------------------
+ * One decode token per sequence through ONE layer of an adjacent pair that
+ * shares k_cache / v_cache (Hymba blog, Hymba 的整体架构: adjacent blocks share
+ * one KV cache; model card 模型使用: generation with use_cache).
+ *
+ * The token sits at position p = n_meta + n_prev (same n_prev for the whole
+ * batch).  Cache rows per sequence: 0..n_meta-1 meta tokens, then cache_slots
+ * ring slots (window > 0: the token after n_prev earlier ones lives in slot
+ * n_meta + n_prev mod window; window <= 0: slot n_meta + n_prev).  K in the
+ * cache is already rotated.
+ *   producer (k_new, v_new != NULL): rotate k_new at p and write k_new/v_new
+ *     to the token's slot, then attend;
+ *   consumer (k_new == v_new == NULL): attend only.
+ * Visible rows: the meta rows and the slots of the last min(n_prev+1, window)
+ * tokens (all n_prev+1 for window <= 0).  conv_state and ssm_state advance by
+ * one token in place; out = branch norm-and-average of the two branches.
+ * Optional ya_out / ys_out ([B, Di] f32) receive the branch outputs.
+ * Supported: bf16 with Dh = 64 (MFMA), f32 with Dh in {16, 32, 64}; N = 16; K = 4.
+ * Workspace: hm_mixer_step_workspace() bytes.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int B, Hq, Hkv, Dh, Di, N, K, n_meta, window, cache_slots;
+  long long n_prev;
+  float rope_base, scale, eps;
+  hm_dtype dtype;
+  const void *q, *k_new, *v_new;           /* [B,Hq,Dh], [B,Hkv,Dh], [B,Hkv,Dh] */
+  void *k_cache, *v_cache;                 /* [B, n_meta+cache_slots, Hkv, Dh] */
+  const void *x, *delta, *Bm, *Cm, *z;     /* [B,Di], [B,Di], [B,N], [B,N], [B,Di] */
+  const float *A, *D, *conv_w, *conv_b;    /* [Di,N], [Di], [Di,K], [Di] */
+  float *conv_state, *ssm_state;           /* [B,Di,K-1], [B,Di,N]   in/out */
+  const float *beta_a, *beta_s;            /* [Di] */
+  void* out;                               /* [B, Di] */
+  float *ya_out, *ys_out;                  /* optional [B, Di] */
+  void* workspace;
+  size_t workspace_bytes;
+} hm_step_args;
+hm_status hm_mixer_step(const hm_step_args* a, void* stream);
+size_t hm_mixer_step_workspace(const hm_step_args* a);
+
+/* ------------------------------------------------------------------------
+ * Index exports, computed by the same device predicates the kernels use.
+ *   hm_debug_attn_mask: out_dev[i*T + j] = 1 if row i may attend row j (u8 [T,T]).
+ *   hm_debug_tile_plan: out_dev[a*nk + c] (int32 [ceil(T/bm), ceil(T/bn)]) =
+ *     0 tile skipped, 1 visited with the element mask, 2 visited unmasked,
+ *     for query tiles of bm rows and key tiles of bn rows (any bm, bn > 0); the
+ *     key-tile walk and classification are the attention kernel's own, and
+ *     hm_debug_attn_tiles() reports the tile sizes the bf16 kernel runs with
+ *     (query rows per workgroup, per wave, and keys per tile).
+ *     cap = number of int32 elements available at out_dev.
+ *   hm_debug_cache_slot: host function, the decode ring slot (-1 if n_prev < 0).
+ * ---------------------------------------------------------------------- */
+hm_status hm_debug_attn_mask(int T, int n_meta, int window, unsigned char* out_dev,
+                             void* stream);
+hm_status hm_debug_tile_plan(int T, int n_meta, int window, int bm, int bn,
+                             int* out_dev, long long cap, void* stream);
+void hm_debug_attn_tiles(int* bm_workgroup, int* bm_wave, int* bn);
+long long hm_debug_cache_slot(long long n_prev, int n_meta, int window);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HM_H_ */

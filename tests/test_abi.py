@@ -1,0 +1,125 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol include/hm.h
+declares, answers its host-side queries, and rejects invalid arguments before
+launching anything (these calls never reach a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hm.h")
+
+hm = pytest.importorskip("hybrid_head_lm_amd")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 18
+    lib = ctypes.CDLL(hm.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) <= set(hm.EXPORTS) | {"hm_abi_version"}
+
+
+def test_version_and_status_strings():
+    assert hm.lib.hm_abi_version() == 1
+    for code, name in enumerate(["HM_OK", "HM_ERR_INVALID", "HM_ERR_UNSUPPORTED",
+                                 "HM_ERR_WORKSPACE", "HM_ERR_HIP"]):
+        assert hm.lib.hm_status_string(code).decode() == name
+
+
+def test_cache_slot_matches_oracle():
+    for n_prev in (0, 1, 5, 1023, 1024, 2048, 99999):
+        for M, W in ((128, 1024), (4, 16), (0, 1), (3, 0)):
+            assert hm.debug_cache_slot(n_prev, M, W) == oracle.cache_slot(n_prev, M, W)
+    assert hm.debug_cache_slot(-1, 1, 1) == -1
+
+
+def test_workspace_queries():
+    L = hm.lib
+    assert L.hm_swa_meta_attn_workspace(1, 2176, 5, 64, hm.HM_BF16) == 2 * 5 * 2176 * 64 * 2
+    assert L.hm_swa_meta_attn_workspace(1, 64, 1, 16, hm.HM_F32) == 64 * 16 * 4
+    assert L.hm_swa_meta_attn_workspace(0, 64, 1, 16, hm.HM_F32) == 0
+    assert L.hm_selective_scan_workspace(1, 2176, 1600, 16) > 0
+    assert L.hm_selective_scan_workspace(1, 2176, 1600, 8) == 0
+    a = hm.StepArgs(B=64, Hq=25, Hkv=5, Dh=64, Di=1600, N=16, K=4, n_meta=128, window=1024,
+                    cache_slots=1024, n_prev=2048, dtype=hm.HM_BF16)
+    nb = L.hm_mixer_step_workspace(ctypes.byref(a))
+    assert nb >= 64 * 1600 * 4 + 64 * 5 * 5 * 5 * 66 * 4
+
+
+FAKE = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: every call below fails validation
+
+
+def _err():
+    return hm.lib.hm_last_error().decode()
+
+
+def test_attention_rejects_bad_arguments():
+    L = hm.lib
+    args = [FAKE, FAKE, FAKE, ctypes.c_void_p(2 << 20), 1, 64, 2, 1, 16, 4, 16, 1e4, 0, 0.0,
+            hm.HM_F32, FAKE, 1 << 30, None]
+    bad = list(args); bad[0] = None
+    assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_INVALID and "q" in _err()
+    bad = list(args); bad[7] = 3                      # Hq % Hkv != 0 (Hq=2, Hkv=3)
+    assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_INVALID
+    bad = list(args); bad[9] = 65                     # n_meta > T
+    assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_INVALID
+    bad = list(args); bad[8] = 48                     # f32 head dim 48
+    assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_UNSUPPORTED
+    bad = list(args); bad[14] = hm.HM_BF16            # bf16 needs Dh = 64
+    assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_UNSUPPORTED
+    bad = list(args); bad[16] = 16                    # short workspace
+    assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_WORKSPACE
+    bad = list(args); bad[3] = FAKE                   # o aliases q
+    assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_INVALID
+    bad = list(args); bad[1] = ctypes.c_void_p((1 << 20) + 4)   # misaligned k
+    assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_INVALID
+
+
+def test_scan_and_conv_reject_bad_arguments():
+    L = hm.lib
+    y = ctypes.c_void_p(3 << 20)
+    assert L.hm_selective_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, y, None,
+                               1, 64, 32, 8, hm.HM_F32, FAKE, 1 << 30, None) == hm.HM_ERR_UNSUPPORTED
+    assert L.hm_selective_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, y, None,
+                               1, 0, 32, 16, hm.HM_F32, FAKE, 1 << 30, None) == hm.HM_ERR_INVALID
+    assert L.hm_selective_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, y, None,
+                               1, 64, 32, 16, hm.HM_F32, FAKE, 4, None) == hm.HM_ERR_WORKSPACE
+    assert L.hm_selective_scan(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None,
+                               1, 64, 32, 16, hm.HM_F32, FAKE, 1 << 30, None) == hm.HM_ERR_INVALID
+    assert L.hm_causal_conv1d(FAKE, FAKE, None, None, y, None, 1, 8, 4, 3, 1, hm.HM_F32,
+                              None) == hm.HM_ERR_UNSUPPORTED
+    assert L.hm_causal_conv1d(None, FAKE, None, None, y, None, 1, 8, 4, 4, 1, hm.HM_F32,
+                              None) == hm.HM_ERR_INVALID
+    assert L.hm_branch_norm_mean(FAKE, FAKE, FAKE, FAKE, -1.0, y, 4, 8, hm.HM_F32,
+                                 None) == hm.HM_ERR_INVALID
+    assert L.hm_branch_norm_mean(FAKE, FAKE, FAKE, FAKE, 1e-6, y, 4, 8, 7, None) == hm.HM_ERR_UNSUPPORTED
+
+
+def test_step_and_prefill_reject_bad_arguments():
+    L = hm.lib
+    a = hm.StepArgs(B=2, Hq=2, Hkv=1, Dh=16, Di=32, N=16, K=4, n_meta=4, window=16,
+                    cache_slots=8, n_prev=3, rope_base=1e4, eps=1e-6, dtype=hm.HM_F32)
+    assert L.hm_mixer_step(ctypes.byref(a), None) == hm.HM_ERR_INVALID      # slots < window
+    a.cache_slots = 16
+    a.Di = 31
+    assert L.hm_mixer_step(ctypes.byref(a), None) == hm.HM_ERR_INVALID      # Di != Hq*Dh
+    a.Di = 32
+    a.N = 8
+    assert L.hm_mixer_step(ctypes.byref(a), None) == hm.HM_ERR_UNSUPPORTED
+    a.N = 16
+    assert L.hm_mixer_step(ctypes.byref(a), None) == hm.HM_ERR_INVALID      # NULL pointers
+    p = hm.PrefillArgs(B=1, T=64, Hq=2, Hkv=1, Dh=16, Di=32, N=16, K=4, n_meta=4, window=16,
+                       rope_base=1e4, eps=1e-6, dtype=hm.HM_F32)
+    assert L.hm_mixer_prefill(ctypes.byref(p), None) == hm.HM_ERR_INVALID   # NULL outputs
+    assert L.hm_mixer_prefill(None, None) == hm.HM_ERR_INVALID

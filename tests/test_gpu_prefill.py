@@ -1,0 +1,204 @@
+"""GPU parity: the HIP prefill path (through the C ABI) against the CPU oracle.
+
+Tolerances: float32 workloads max|g - r| <= 1e-4 max|r| per output tensor;
+bf16-input / fp32-accumulate workloads max|g - r| <= 2e-2 max|r|; the mask,
+tile plan and ring slot bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import GLOBAL_PREFILL, SWA_PREFILL, TINY, prefill_inputs, with_
+
+pytestmark = pytest.mark.gpu
+
+hm = pytest.importorskip("hybrid_head_lm_amd")
+torch = pytest.importorskip("torch")
+from gpu_util import assert_close, down, up, up_inputs  # noqa: E402
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# ------------------------------------------------------------------ index exports
+MASK_CASES = [(64, 4, 16), (1, 0, 0), (2, 1, 1), (100, 0, 7), (130, 128, 0), (300, 16, 100),
+              (257, 3, 256), (2176, 128, 1024)]
+
+
+@pytest.mark.parametrize("T,M,W", MASK_CASES)
+def test_mask_bit_exact(T, M, W):
+    got = hm.debug_attn_mask(T, M, W).cpu().numpy().astype(bool)
+    assert np.array_equal(got, oracle.mask(T, M, W))
+
+
+TILE_CASES = [(64, 4, 16), (300, 16, 100), (2176, 128, 1024), (8320, 128, 0), (1000, 5, 63),
+              (129, 128, 1), (257, 0, 64), (16512, 128, 1024)]
+
+
+@pytest.mark.parametrize("T,M,W", TILE_CASES)
+def test_tile_plan_bit_exact(T, M, W):
+    bmw, bmv, bn = hm.debug_attn_tiles()
+    for bm, bnn in ((bmw, bn), (bmv, bn), (7, 5), (1, 1) if T <= 300 else (bmw, bn)):
+        got = hm.debug_tile_plan(T, M, W, bm, bnn).cpu().numpy()
+        assert np.array_equal(got, oracle.tile_kinds(T, M, W, bm, bnn)), (bm, bnn)
+
+
+# ------------------------------------------------------------------ attention
+def _attn_case(shape, seed, rows=None):
+    inp = prefill_inputs(shape, seed)
+    t = up_inputs(inp, shape.dtype)
+    o = hm.swa_meta_attn(t["q"], t["k"], t["v"], shape.M, shape.W, shape.rope_base)
+    torch.cuda.synchronize()
+    got = down(o)
+    ref = oracle.attention(inp["q"], inp["k"], inp["v"], shape.M, shape.W, shape.rope_base,
+                           rows=rows)
+    if rows is not None:
+        got = got[:, rows]
+    return got, ref
+
+
+def test_attention_tiny_f32():
+    got, ref = _attn_case(TINY, 0)
+    assert_close(got, ref, "f32", "attention tiny")
+
+
+@pytest.mark.parametrize("Dh", [16, 32, 64])
+def test_attention_f32_head_dims(Dh):
+    shape = with_(TINY, B=2, N=90, Dh=Dh, Hq=4, Hkv=2, W=20, M=6, Di=4 * Dh)
+    got, ref = _attn_case(shape, 1)
+    assert_close(got, ref, "f32", f"attention f32 Dh={Dh}")
+
+
+BF16_CASES = [
+    # (B, M, N, Hq, Hkv, W): several 128-row query tiles, ragged tails, meta
+    # prefixes that end inside a key tile, global and windowed, GQA groups
+    (1, 4, 60, 2, 1, 16),
+    (2, 16, 284, 10, 2, 100),
+    (1, 0, 300, 5, 5, 0),
+    (1, 3, 200, 4, 1, 1),
+    (1, 128, 2048, 25, 5, 1024),
+    (1, 70, 450, 6, 3, 64),
+]
+
+
+@pytest.mark.parametrize("B,M,N,Hq,Hkv,W", BF16_CASES)
+def test_attention_bf16(B, M, N, Hq, Hkv, W):
+    shape = with_(SWA_PREFILL, B=B, M=M, N=N, Hq=Hq, Hkv=Hkv, W=W, Di=Hq * 64)
+    got, ref = _attn_case(shape, 2)
+    assert_close(got, ref, "bf16", "attention bf16")
+
+
+def test_attention_bf16_global_full_size_sampled_rows():
+    # the global-attention workload at full size (B=4, T=8320), rows sampled
+    # across tile boundaries, the meta prefix and the end
+    shape = GLOBAL_PREFILL
+    rows = sorted(set([0, 1, 63, 64, 127, 128, 129, 255, 1000, 4095, 4096, 6000, 8191, 8318,
+                       8319] + list(np.random.default_rng(0).integers(0, shape.T, 17))))
+    got, ref = _attn_case(shape, 3, rows=rows)
+    assert_close(got, ref, "bf16", "attention global full size")
+
+
+# ------------------------------------------------------------------ conv / scan / norm
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 2, 5, 64, 200])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_causal_conv1d(dtype, T, with_state):
+    rng = np.random.default_rng(T)
+    B, Di = 2, 96
+    from workloads import bf16_round
+    x = rng.standard_normal((B, T, Di)).astype(np.float32)
+    if dtype == "bf16":
+        x = bf16_round(x)
+    w = (rng.standard_normal((Di, 4)) / 2).astype(np.float32)
+    b = (0.1 * rng.standard_normal(Di)).astype(np.float32)
+    s0 = rng.standard_normal((B, Di, 3)).astype(np.float32) if with_state else None
+    so = torch.empty((B, Di, 3), dtype=torch.float32, device="cuda")
+    y = hm.causal_conv1d(up(x, dtype), up(w, "f32"), up(b, "f32"),
+                         None if s0 is None else up(s0, "f32"), True, state_out=so)
+    ref, ref_st = oracle.causal_conv1d(x, w, b, s0, True)
+    assert_close(down(y), ref, dtype, "conv y")
+    assert np.array_equal(down(so), ref_st), "conv state_out must be the exact inputs"
+
+
+def _scan_inputs(shape, seed):
+    inp = prefill_inputs(shape, seed)
+    rng = np.random.default_rng(seed + 100)
+    h0 = rng.standard_normal((shape.B, shape.Di, 16)).astype(np.float32)
+    return inp, h0
+
+
+@pytest.mark.parametrize("shape", [TINY, with_(TINY, dtype="bf16"),
+                                   with_(SWA_PREFILL, N=2048, M=128),
+                                   with_(SWA_PREFILL, B=3, N=777, M=11, Di=200, Hq=1, Dh=200)],
+                         ids=["tiny-f32", "tiny-bf16", "swa-full", "ragged"])
+@pytest.mark.parametrize("use_h0,use_dz", [(False, True), (True, True), (True, False)])
+def test_selective_scan(shape, use_h0, use_dz):
+    inp, h0 = _scan_inputs(shape, 5)
+    dt = shape.dtype
+    t = up_inputs(inp, dt)
+    h_out = torch.empty((shape.B, shape.Di, 16), dtype=torch.float32, device="cuda")
+    y = hm.selective_scan(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"],
+                          t["D"] if use_dz else None, t["z"] if use_dz else None,
+                          up(h0, "f32") if use_h0 else None, h_out=h_out)
+    ref, ref_h = oracle.selective_scan(inp["x"], inp["delta"], inp["A"], inp["Bm"], inp["Cm"],
+                                       inp["D"] if use_dz else None, inp["z"] if use_dz else None,
+                                       h0 if use_h0 else None)
+    assert_close(down(y), ref, dt, "scan y")
+    assert_close(down(h_out), ref_h, dt, "scan h_out")
+
+
+@pytest.mark.parametrize("shape", [TINY, with_(SWA_PREFILL, N=2048, M=128),
+                                   with_(SWA_PREFILL, B=2, N=500, M=7, Di=320, Hq=5)],
+                         ids=["tiny-f32", "swa-full", "ragged"])
+@pytest.mark.parametrize("use_state", [False, True])
+def test_conv_selective_scan(shape, use_state):
+    inp, h0 = _scan_inputs(shape, 6)
+    rng = np.random.default_rng(7)
+    cs0 = rng.standard_normal((shape.B, shape.Di, 3)).astype(np.float32) if use_state else None
+    dt = shape.dtype
+    t = up_inputs(inp, dt)
+    h_out = torch.empty((shape.B, shape.Di, 16), dtype=torch.float32, device="cuda")
+    cs_out = torch.empty((shape.B, shape.Di, 3), dtype=torch.float32, device="cuda")
+    y = hm.conv_selective_scan(t["x"], t["conv_w"], t["conv_b"], t["delta"], t["A"], t["Bm"],
+                               t["Cm"], t["D"], t["z"],
+                               conv_state_in=None if cs0 is None else up(cs0, "f32"),
+                               conv_state_out=cs_out, h0=up(h0, "f32") if use_state else None,
+                               h_out=h_out)
+    xc, ref_cs = oracle.causal_conv1d(inp["x"], inp["conv_w"], inp["conv_b"], cs0, True)
+    ref, ref_h = oracle.selective_scan(xc, inp["delta"], inp["A"], inp["Bm"], inp["Cm"], inp["D"],
+                                       inp["z"], h0 if use_state else None)
+    assert_close(down(y), ref, dt, "conv+scan y")
+    assert_close(down(h_out), ref_h, dt, "conv+scan h_out")
+    assert np.array_equal(down(cs_out), ref_cs)
+
+
+@pytest.mark.parametrize("dtype,width,rows", [("f32", 32, 64), ("bf16", 1600, 2176),
+                                              ("bf16", 1600, 3), ("f32", 37, 5),
+                                              ("bf16", 200, 9)])
+def test_branch_norm_mean(dtype, width, rows):
+    rng = np.random.default_rng(width)
+    from workloads import bf16_round
+    ya = (0.3 * rng.standard_normal((rows, width))).astype(np.float32)
+    ys = (30 * rng.standard_normal((rows, width))).astype(np.float32)
+    if dtype == "bf16":
+        ya, ys = bf16_round(ya), bf16_round(ys)
+    ba = (1 + 0.1 * rng.standard_normal(width)).astype(np.float32)
+    bs = (1 + 0.1 * rng.standard_normal(width)).astype(np.float32)
+    out = hm.branch_norm_mean(up(ya, dtype), up(ys, dtype), up(ba, "f32"), up(bs, "f32"), 1e-6)
+    ref = oracle.branch_norm_mean(ya, ys, ba, bs, 1e-6)
+    assert_close(down(out), ref, dtype, "norm-mean")
+
+
+# ------------------------------------------------------------------ whole layer
+@pytest.mark.parametrize("shape", [TINY, SWA_PREFILL], ids=["tiny-f32", "swa-prefill-full"])
+def test_mixer_prefill(shape):
+    inp = prefill_inputs(shape, 0)
+    t = up_inputs(inp, shape.dtype)
+    r = hm.mixer_prefill(t, shape.M, shape.W, rope_base=shape.rope_base, eps=shape.eps)
+    torch.cuda.synchronize()
+    ref = oracle.mixer_prefill(inp, shape.M, shape.W, shape.rope_base, shape.eps)
+    for k in ("ya", "ys", "out", "ssm_state"):
+        assert_close(down(r[k]), ref[k], shape.dtype, f"mixer {k}")
+    assert np.array_equal(down(r["conv_state"]), ref["conv_state"])

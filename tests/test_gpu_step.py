@@ -1,0 +1,83 @@
+"""GPU parity of the decode step (one token, a KV-sharing pair of layers).
+
+Producer then consumer on one shared cache, compared with the oracle's step on
+the same inputs: output, both branch outputs, the advanced conv/SSM states and
+the cache row the producer writes.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from workloads import DECODE_PAIR, TINY, decode_inputs, with_
+
+pytestmark = pytest.mark.gpu
+
+hm = pytest.importorskip("hybrid_head_lm_amd")
+torch = pytest.importorskip("torch")
+from gpu_util import assert_close, down, up_inputs  # noqa: E402
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _run_pair(shape, seed):
+    d = decode_inputs(shape, seed)
+    t = up_inputs(d, shape.dtype)
+    kc, vc = t["k_cache"], t["v_cache"]
+    pa = hm.StepPlan(t["a"], kc, vc, shape.n_prev, shape.M, shape.W, rope_base=shape.rope_base,
+                     eps=shape.eps, want_branches=True)
+    pb = hm.StepPlan(t["b"], kc, vc, shape.n_prev, shape.M, shape.W, rope_base=shape.rope_base,
+                     eps=shape.eps, want_branches=True)
+    pa.run()
+    pb.run()
+    torch.cuda.synchronize()
+    ra = oracle.mixer_step(d["a"], d["k_cache"], d["v_cache"], shape.n_prev, shape.M, shape.W,
+                           producer=True, rope_base=shape.rope_base, eps=shape.eps)
+    rb = oracle.mixer_step(d["b"], ra["k_cache"], ra["v_cache"], shape.n_prev, shape.M, shape.W,
+                           producer=False, rope_base=shape.rope_base, eps=shape.eps)
+    return d, t, (pa, pb), (ra, rb)
+
+
+def _check(shape, seed):
+    d, t, plans, refs = _run_pair(shape, seed)
+    dt = shape.dtype
+    for name, plan, ref in zip("ab", plans, refs):
+        assert_close(down(plan.out), ref["out"], dt, f"{name} out")
+        assert_close(down(plan.ya), ref["ya"], dt, f"{name} ya")
+        assert_close(down(plan.ys), ref["ys"], dt, f"{name} ys")
+        assert_close(down(t[name]["ssm_state"]), ref["ssm_state"], dt, f"{name} ssm_state")
+        assert np.array_equal(down(t[name]["conv_state"]), ref["conv_state"]), f"{name} conv"
+    slot = oracle.cache_slot(shape.n_prev, shape.M, shape.W)
+    assert hm.debug_cache_slot(shape.n_prev, shape.M, shape.W) == slot
+    kc = down(t["k_cache"])
+    vc = down(t["v_cache"])
+    assert_close(kc[:, slot], refs[0]["k_cache"][:, slot], dt, "written K row")
+    assert np.array_equal(vc[:, slot], refs[0]["v_cache"][:, slot])
+    # every other row is untouched
+    others = [r for r in range(kc.shape[1]) if r != slot]
+    assert np.array_equal(kc[:, others], d["k_cache"][:, others].astype(np.float64))
+
+
+def test_decode_pair_full_size():
+    _check(DECODE_PAIR, 0)
+
+
+@pytest.mark.parametrize("n_prev", [0, 1, 63, 64, 300, 1023, 1024, 1025, 5000])
+def test_decode_pair_bf16_window_positions(n_prev):
+    shape = with_(DECODE_PAIR, B=3, n_prev=n_prev)
+    _check(shape, n_prev)
+
+
+@pytest.mark.parametrize("n_prev", [0, 5, 200])
+def test_decode_pair_bf16_global(n_prev):
+    shape = with_(DECODE_PAIR, B=2, W=0, cache_slots=256, n_prev=n_prev, M=30)
+    _check(shape, 11 + n_prev)
+
+
+@pytest.mark.parametrize("n_prev", [0, 5, 15, 16, 40])
+@pytest.mark.parametrize("Dh", [16, 64])
+def test_decode_pair_f32(n_prev, Dh):
+    shape = with_(TINY, B=2, n_prev=n_prev, cache_slots=16, Dh=Dh, Di=2 * Dh)
+    _check(shape, 3)
