@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the Hymba hybrid-head mixer core on one MI355X.
+
+A step is one prefill pass of one mixer layer (RoPE, the meta + sliding-window
+GQA attention, the causal conv + selective scan branch, the branch norm and
+average) over the sliding-window workload: batch 1, 128 meta + 2048 tokens,
+25 query heads x 64, 5 KV heads, window 1024, SSM width 1600 x 16 states,
+bf16 inputs with float32 accumulation, synthetic seeded inputs resident in HBM.
+`value` is prefill tokens/s per layer (B * (M + N) rows / step time).
+
+Also reported on the same JSON line:
+  roofline      the attention kernel (the dominant one) timed on its own with
+                HIP events on its stream: algorithmic FLOPs / time vs the bf16
+                MFMA peak;
+  decode        one token for 64 sequences through an adjacent pair of layers
+                that share a 128 + 1024-row KV cache: steps/s and HBM fraction;
+  global_prefill, stack
+                the global-attention layer (batch 4, 128 + 8192 tokens) and the
+                32-layer stack (batch 2, 128 + 16384 tokens, layers 0/15/31
+                global, adjacent sliding-window layers sharing prepared K/V);
+  cpu_baseline  the float64 CPU oracle on one whole layer of the step's workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def attn_flops(shape) -> float:
+    """4 * Dh * Hq * B * (visible (query, key) pairs per head) — QK^T and PV only."""
+    import numpy as np
+    i = np.arange(shape.T, dtype=np.int64)
+    vis = np.minimum(i + 1, shape.M + shape.W) if shape.W > 0 else i + 1
+    return 4.0 * shape.Dh * shape.Hq * shape.B * float(vis.sum())
+
+
+def scan_bytes(shape) -> float:
+    """Compulsory HBM bytes of the SSM branch: read x, delta, z, write y (2 B each
+    per token-channel), read B and C (2 B per token-state), A, D, conv params once."""
+    tc = shape.B * shape.T * shape.Di
+    return 8.0 * tc + 4.0 * shape.B * shape.T * shape.Ns + 4.0 * shape.Di * (shape.Ns + 1 + 5)
+
+
+def decode_bytes(shape) -> float:
+    """Compulsory HBM bytes of one decode token through a producer + consumer
+    layer: both read the visible cache rows (K and V), each reads and writes its
+    SSM and conv states, reads q, x, delta, z, B, C and writes out; the producer
+    reads k_new, v_new and writes them into the cache."""
+    B, Hkv, Dh, Di, Ns = shape.B, shape.Hkv, shape.Dh, shape.Di, shape.Ns
+    vis = shape.M + (min(shape.n_prev + 1, shape.W) if shape.W > 0 else shape.n_prev + 1)
+    per_layer = (B * vis * Hkv * Dh * 2 * 2            # K and V rows
+                 + B * Di * Ns * 4 * 2                 # SSM state read + write
+                 + B * Di * 3 * 4 * 2                  # conv state read + write
+                 + B * shape.Hq * Dh * 2               # q
+                 + B * Di * 2 * 4                      # x, delta, z, out
+                 + B * Ns * 2 * 2)                     # B, C
+    producer = B * Hkv * Dh * 2 * 2 * 2                # k_new, v_new read + written
+    return 2.0 * per_layer + producer
+
+
+def _file_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src: str, summary: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != _file_hash(os.path.join(ROOT, kernel_src)):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def timed(fn, steps: int, warmup: int, stream=None):
+    """Mean milliseconds per call over `steps` calls, HIP events on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = stream or torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(shape, inp):
+    """The oracle (float64 NumPy) on one whole prefill layer of the workload."""
+    import oracle
+    threads = None
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((d.get("num_threads") or 1) for d in info) if info else 1
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    oracle.mixer_prefill(inp, shape.M, shape.W, shape.rope_base, shape.eps)
+    dt = time.perf_counter() - t0
+    return {"value": shape.B * shape.T / dt, "unit": "tokens/s", "cores": threads or 1,
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"one whole prefill layer of {shape.name} (float64 NumPy), "
+                      f"{dt:.2f} s"}
+
+
+def run_prefill(shape, hm, t, steps, warmup, two_streams):
+    import torch
+    s2 = torch.cuda.Stream() if two_streams else None
+    plan = hm.PrefillPlan(t, shape.M, shape.W, rope_base=shape.rope_base, eps=shape.eps,
+                          want_states=False, stream2=s2)
+    ms = timed(plan.run, steps, warmup)
+    return plan, ms
+
+
+def run_stack(shape, hm, steps, warmup):
+    """32 layers; sliding-window pairs share the producer's prepared K/V."""
+    import torch
+    from workloads import prefill_inputs_torch, stack_layer_roles
+    roles = stack_layer_roles(shape)
+    layers = []
+    for layer, (_, src) in enumerate(roles):
+        t = prefill_inputs_torch(shape, 0, layer, torch.device("cuda"))
+        if src != layer:
+            del t["k"], t["v"]
+        layers.append(t)
+    s2 = torch.cuda.Stream()
+    stack = hm.StackPlan(layers, roles, shape.M, shape.rope_base, shape.eps, stream2=s2)
+    ms = timed(stack.run, steps, warmup)
+    return ms, len(roles)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quick", action="store_true", help="skip the global-prefill and stack lines")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the mixer core runs on a single MI355X here "
+              "(no multi-GPU path); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import hybrid_head_lm_amd as hm
+    from workloads import (DECODE_PAIR, GLOBAL_PREFILL, STACK, SWA_PREFILL, decode_inputs,
+                           prefill_inputs, to_device)
+
+    torch.cuda.set_device(0)
+    shape = SWA_PREFILL
+    inp = prefill_inputs(shape, 0)
+    t = to_device(inp, shape.dtype)
+
+    # the step: one mixer layer, both head types on two streams
+    plan, ms = run_prefill(shape, hm, t, args.steps, args.warmup, two_streams=True)
+    _, ms_serial = run_prefill(shape, hm, t, args.steps, args.warmup, two_streams=False)
+    tokens = shape.B * shape.T
+
+    # dominant kernel on its own: attention over the prepared K/V
+    ms_attn = timed(lambda: hm.attn_with_kv(t["q"], plan.kv, shape.Hkv, shape.M, shape.W,
+                                            shape.rope_base, out=plan.ya),
+                    args.steps, args.warmup)
+    fl = attn_flops(shape)
+    achieved = fl / (ms_attn * 1e-3) / 1e12
+    traffic = traffic_from_profile("hybrid_head_lm_amd/csrc/attn.hip",
+                                   "attn_fwd_bf16.swa-prefill.pmc.txt")
+
+    # SSM branch and fusion on their own (context for the breakdown)
+    ms_ssm = timed(lambda: hm.conv_selective_scan(t["x"], t["conv_w"], t["conv_b"], t["delta"],
+                                                  t["A"], t["Bm"], t["Cm"], t["D"], t["z"],
+                                                  out=plan.ys), args.steps, args.warmup)
+    ms_norm = timed(lambda: hm.branch_norm_mean(plan.ya, plan.ys, t["beta_a"], t["beta_s"],
+                                                shape.eps, out=plan.out), args.steps, args.warmup)
+
+    # decode: one token through the producer / consumer pair
+    dshape = DECODE_PAIR
+    d = to_device(decode_inputs(dshape, 0), dshape.dtype)
+    pa = hm.StepPlan(d["a"], d["k_cache"], d["v_cache"], dshape.n_prev, dshape.M, dshape.W,
+                     rope_base=dshape.rope_base, eps=dshape.eps)
+    pb = hm.StepPlan(d["b"], d["k_cache"], d["v_cache"], dshape.n_prev, dshape.M, dshape.W,
+                     rope_base=dshape.rope_base, eps=dshape.eps)
+
+    def decode_step():
+        pa.run()
+        pb.run()
+    ms_dec = timed(decode_step, args.steps, args.warmup)
+    dbytes = decode_bytes(dshape)
+
+    result = {
+        "metric": "hybrid-mixer prefill tokens/s per layer + decode steps/s; % MFMA/HBM roofline",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": shape.name, "batch": shape.B, "meta_tokens": shape.M,
+                   "tokens": shape.N, "rows": shape.T, "q_heads": shape.Hq,
+                   "kv_heads": shape.Hkv, "head_dim": shape.Dh, "window": shape.W,
+                   "ssm_width": shape.Di, "ssm_states": shape.Ns, "conv": shape.K,
+                   "branches": "attention and SSM on two streams"},
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "algorithmic_flop_per_launch": fl, "ms_per_launch": ms_attn},
+        "breakdown_ms": {"layer_two_streams": ms, "layer_one_stream": ms_serial,
+                         "attention_kernel": ms_attn, "ssm_branch": ms_ssm,
+                         "norm_mean": ms_norm},
+        "ssm_branch": {"bound": "hbm", "achieved": scan_bytes(shape) / (ms_ssm * 1e-3) / 1e9,
+                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                       "frac": scan_bytes(shape) / (ms_ssm * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+        "decode": {"workload": dshape.name, "steps_per_s": 1e3 / ms_dec,
+                   "tokens_per_s": dshape.B * 1e3 / ms_dec, "ms_per_step": ms_dec,
+                   "roofline": {"bound": "hbm", "achieved": dbytes / (ms_dec * 1e-3) / 1e9,
+                                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                "frac": dbytes / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                "algorithmic_bytes_per_step": dbytes}},
+    }
+    del pa, pb, d
+
+    if not args.quick:
+        gshape = GLOBAL_PREFILL
+        gt = to_device(prefill_inputs(gshape, 0), gshape.dtype)
+        gsteps = max(3, args.steps // 5)
+        gplan, gms = run_prefill(gshape, hm, gt, gsteps, 2, two_streams=True)
+        gms_attn = timed(lambda: hm.attn_with_kv(gt["q"], gplan.kv, gshape.Hkv, gshape.M,
+                                                 gshape.W, gshape.rope_base, out=gplan.ya),
+                         gsteps, 2)
+        gfl = attn_flops(gshape)
+        result["global_prefill"] = {
+            "workload": gshape.name, "tokens_per_s": gshape.B * gshape.T / (gms * 1e-3),
+            "ms_per_layer": gms, "attention_tflops": gfl / (gms_attn * 1e-3) / 1e12,
+            "attention_frac_mfma": gfl / (gms_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        del gt, gplan
+        torch.cuda.empty_cache()
+        sms, nl = run_stack(STACK, hm, 3, 1)
+        result["stack"] = {"workload": STACK.name, "layers": nl,
+                           "tokens_per_s_per_layer": STACK.B * STACK.T * nl / (sms * 1e-3),
+                           "ms_per_stack": sms,
+                           "inputs": "torch Philox generator on the device (same distributions)"}
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(shape, inp)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -25,6 +25,7 @@ HM_F32, HM_BF16 = 0, 1
 EXPORTS = (
     "hm_abi_version", "hm_status_string", "hm_last_error",
     "hm_swa_meta_attn", "hm_swa_meta_attn_workspace",
+    "hm_attn_kv_bytes", "hm_attn_kv_prepare", "hm_attn_with_kv",
     "hm_causal_conv1d", "hm_selective_scan", "hm_selective_scan_workspace",
     "hm_conv_selective_scan", "hm_branch_norm_mean",
     "hm_mixer_prefill", "hm_mixer_prefill_workspace",
@@ -51,7 +52,9 @@ class PrefillArgs(ctypes.Structure):
         ("pos0", _ll), ("rope_base", _f), ("scale", _f), ("eps", _f), ("dtype", _i),
     ] + [(n, _vp) for n in ("q", "k", "v", "x", "delta", "Bm", "Cm", "z", "A", "D", "conv_w",
                             "conv_b", "beta_a", "beta_s", "ya", "ys", "out", "conv_state_out",
-                            "h_out", "workspace")] + [("workspace_bytes", _sz)]
+                            "h_out", "kv")] + [("kv_bytes", _sz), ("kv_reuse", _i),
+                                               ("stream2", _vp), ("workspace", _vp),
+                                               ("workspace_bytes", _sz)]
 
 
 class StepArgs(ctypes.Structure):
@@ -79,6 +82,11 @@ def _load():
                                      _i, _vp, _sz, _vp]
     lib.hm_swa_meta_attn_workspace.argtypes = [_i, _i, _i, _i, _i]
     lib.hm_swa_meta_attn_workspace.restype = _sz
+    lib.hm_attn_kv_bytes.argtypes = [_i, _i, _i, _i, _i]
+    lib.hm_attn_kv_bytes.restype = _sz
+    lib.hm_attn_kv_prepare.argtypes = [_vp, _vp, _vp, _sz, _i, _i, _i, _i, _f, _ll, _i, _vp]
+    lib.hm_attn_with_kv.argtypes = [_vp, _vp, _sz, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _ll, _f,
+                                    _i, _vp]
     lib.hm_causal_conv1d.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
     lib.hm_selective_scan.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i,
                                       _i, _i, _i, _vp, _sz, _vp]
@@ -106,3 +114,4 @@ if lib.hm_abi_version() != 1:
     raise ImportError("libhm ABI version mismatch")
 
 from .api import *  # noqa: E402,F401,F403
+from .stack import StackPlan  # noqa: E402,F401

@@ -14,7 +14,7 @@ import torch
 from . import HM_BF16, HM_F32, HmError, PrefillArgs, StepArgs, lib
 
 __all__ = [
-    "swa_meta_attn", "causal_conv1d", "selective_scan", "conv_selective_scan",
+    "swa_meta_attn", "attn_kv_bytes", "attn_kv_prepare", "attn_with_kv", "causal_conv1d", "selective_scan", "conv_selective_scan",
     "branch_norm_mean", "mixer_prefill", "PrefillPlan", "mixer_step", "StepPlan",
     "debug_attn_mask", "debug_tile_plan", "debug_attn_tiles", "debug_cache_slot",
     "dtype_code",
@@ -81,6 +81,37 @@ def swa_meta_attn(q, k, v, n_meta: int, window: int, rope_base: float = 10000.0,
     ws = workspace if workspace is not None else _ws(nb, dev)
     _check(lib.hm_swa_meta_attn(_p(q), _p(k), _p(v), _p(out), B, T, Hq, Hkv, Dh, n_meta, window,
                                 rope_base, pos0, scale, dt, _p(ws), ws.numel(), _stream()))
+    return out
+
+
+def attn_kv_bytes(B: int, T: int, Hkv: int, Dh: int, dtype) -> int:
+    code = dtype if isinstance(dtype, int) else (HM_BF16 if dtype == torch.bfloat16 else HM_F32)
+    return lib.hm_attn_kv_bytes(B, T, Hkv, Dh, code)
+
+
+def attn_kv_prepare(k, v, rope_base: float = 10000.0, pos0: int = 0, kv=None):
+    """Rotate k and lay out k, v for the attention kernel; returns the kv buffer."""
+    dev = _dev(k, v, kv)
+    B, T, Hkv, Dh = k.shape
+    dt = dtype_code(k)
+    nb = lib.hm_attn_kv_bytes(B, T, Hkv, Dh, dt)
+    if kv is None:
+        kv = _ws(nb, dev)
+    _check(lib.hm_attn_kv_prepare(_p(k), _p(v), _p(kv), kv.numel() * kv.element_size(), B, T,
+                                  Hkv, Dh, rope_base, pos0, dt, _stream()))
+    return kv
+
+
+def attn_with_kv(q, kv, Hkv: int, n_meta: int, window: int, rope_base: float = 10000.0,
+                 pos0: int = 0, scale: float = 0.0, out=None):
+    """Attention of q over a buffer filled by attn_kv_prepare (same rope_base, pos0)."""
+    _dev(q, kv, out)
+    B, T, Hq, Dh = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.hm_attn_with_kv(_p(q), _p(kv), kv.numel() * kv.element_size(), _p(out), B, T, Hq,
+                               Hkv, Dh, n_meta, window, rope_base, pos0, scale, dtype_code(q),
+                               _stream()))
     return out
 
 
@@ -155,10 +186,16 @@ class PrefillPlan:
 
     def __init__(self, t: dict, n_meta: int, window: int, rope_base: float = 10000.0,
                  eps: float = 1e-6, pos0: int = 0, scale: float = 0.0, want_states=True,
-                 out=None, ya=None, ys=None, workspace=None):
+                 out=None, ya=None, ys=None, workspace=None, kv=None, kv_reuse=False,
+                 stream2=None):
+        """kv: prepared K/V buffer (allocated here when None).  kv_reuse: read
+        kv as prepared by an earlier layer (t["k"], t["v"] are then unused).
+        stream2: a torch stream on which the SSM branch runs concurrently."""
         q = t["q"]
-        dev = _dev(*[t[k] for k in ("q", "k", "v", "x", "delta", "Bm", "Cm", "z", "A", "D",
+        dev = _dev(*[t[k] for k in ("q", "x", "delta", "Bm", "Cm", "z", "A", "D",
                                      "conv_w", "conv_b", "beta_a", "beta_s")])
+        if not kv_reuse:
+            _dev(t["k"], t["v"])
         _f32(t["A"], t["D"], t["conv_w"], t["conv_b"], t["beta_a"], t["beta_s"])
         B, T, Hq, Dh = q.shape
         Di = t["x"].shape[2]
@@ -172,12 +209,21 @@ class PrefillPlan:
                                           device=dev)
             self.h = torch.empty((B, Di, t["A"].shape[1]), dtype=torch.float32, device=dev)
         a = PrefillArgs()
-        a.B, a.T, a.Hq, a.Hkv, a.Dh, a.Di = B, T, Hq, t["k"].shape[2], Dh, Di
+        Hkv = t["Hkv"] if "Hkv" in t else t["k"].shape[2]
+        a.B, a.T, a.Hq, a.Hkv, a.Dh, a.Di = B, T, Hq, Hkv, Dh, Di
         a.N, a.K, a.n_meta, a.window = t["A"].shape[1], t["conv_w"].shape[1], n_meta, window
         a.pos0, a.rope_base, a.scale, a.eps, a.dtype = pos0, rope_base, scale, eps, dtype_code(q)
-        for k in ("q", "k", "v", "x", "delta", "Bm", "Cm", "z", "A", "D", "conv_w", "conv_b",
+        for k in ("q", "x", "delta", "Bm", "Cm", "z", "A", "D", "conv_w", "conv_b",
                   "beta_a", "beta_s"):
             setattr(a, k, t[k].data_ptr())
+        if not kv_reuse:
+            a.k, a.v = t["k"].data_ptr(), t["v"].data_ptr()
+        if kv is None:
+            kv = _ws(lib.hm_attn_kv_bytes(B, T, Hkv, Dh, dtype_code(q)), dev)
+        self.kv = kv
+        a.kv, a.kv_bytes, a.kv_reuse = kv.data_ptr(), kv.numel() * kv.element_size(), int(kv_reuse)
+        self.stream2 = stream2
+        a.stream2 = stream2.cuda_stream if stream2 is not None else None
         a.ya, a.ys, a.out = self.ya.data_ptr(), self.ys.data_ptr(), self.out.data_ptr()
         a.conv_state_out = self.conv_state.data_ptr() if want_states else None
         a.h_out = self.h.data_ptr() if want_states else None

@@ -17,6 +17,29 @@ hm_status fail(hm_status s, const std::string& msg) {
   return s;
 }
 
+// Order a second stream after the first (fork) or the first after the second
+// (join) with one cached event per device and direction.  No host
+// synchronisation; the events are created once per thread and device.
+hm_status fork_join(hipStream_t main, hipStream_t side, bool fork) {
+  struct Ev { int dev = -1; hipEvent_t e[2] = {nullptr, nullptr}; };
+  static thread_local Ev cache[16];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16)
+    return fail(HM_ERR_HIP, "hipGetDevice failed or device index >= 16");
+  Ev& c = cache[dev];
+  if (c.dev != dev) {
+    for (int i = 0; i < 2; ++i)
+      if (hipEventCreateWithFlags(&c.e[i], hipEventDisableTiming) != hipSuccess)
+        return fail(HM_ERR_HIP, "hipEventCreateWithFlags failed");
+    c.dev = dev;
+  }
+  hipEvent_t e = c.e[fork ? 0 : 1];
+  hipStream_t from = fork ? main : side, to = fork ? side : main;
+  if (hipEventRecord(e, from) != hipSuccess || hipStreamWaitEvent(to, e, 0) != hipSuccess)
+    return fail(HM_ERR_HIP, "event record / stream wait failed");
+  return HM_OK;
+}
+
 hm_status check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess)
@@ -43,13 +66,13 @@ const char* hm_status_string(hm_status s) {
 
 const char* hm_last_error(void) { return hm::g_last_error.c_str(); }
 
-// Workspace of one prefill layer: the attention scratch followed by the scan
-// scratch (each 256-byte aligned).
+// Workspace of one prefill layer: the scan scratch, then (when the caller gives
+// no kv buffer) the prepared K/V, each 256-byte aligned.
 size_t hm_mixer_prefill_workspace(const hm_prefill_args* a) {
   if (!a) return 0;
-  size_t wa = hm_swa_meta_attn_workspace(a->B, a->T, a->Hkv, a->Dh, a->dtype);
-  size_t ws = hm_selective_scan_workspace(a->B, a->T, a->Di, a->N);
-  return hm::align_up(wa, 256) + hm::align_up(ws, 256);
+  size_t ws = hm::align_up(hm_selective_scan_workspace(a->B, a->T, a->Di, a->N), 256);
+  if (a->kv == nullptr) ws += hm::align_up(hm_attn_kv_bytes(a->B, a->T, a->Hkv, a->Dh, a->dtype), 256);
+  return ws;
 }
 
 hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream) {
@@ -60,25 +83,43 @@ hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream) {
   HM_PTR(a->out);
   HM_REQUIRE(a->ya != a->ys && a->ya != a->out && a->ys != a->out, HM_ERR_INVALID,
              "ya, ys and out must be distinct buffers");
-  size_t need = hm_mixer_prefill_workspace(a);
-  HM_REQUIRE(a->workspace != nullptr && a->workspace_bytes >= need, HM_ERR_WORKSPACE,
-             "workspace smaller than hm_mixer_prefill_workspace()");
-  size_t wa = hm::align_up(hm_swa_meta_attn_workspace(a->B, a->T, a->Hkv, a->Dh, a->dtype), 256);
+  HM_REQUIRE(!a->kv_reuse || a->kv != nullptr, HM_ERR_INVALID, "kv_reuse needs a kv buffer");
+  const size_t need = hm_mixer_prefill_workspace(a);
+  HM_REQUIRE(a->workspace != nullptr && a->workspace_bytes >= need && hm::aligned16(a->workspace),
+             HM_ERR_WORKSPACE, "workspace smaller than hm_mixer_prefill_workspace()");
+  const size_t wscan = hm::align_up(hm_selective_scan_workspace(a->B, a->T, a->Di, a->N), 256);
   char* ws = (char*)a->workspace;
+  void* kv = a->kv ? a->kv : (void*)(ws + wscan);
+  const size_t kvb = a->kv ? a->kv_bytes : a->workspace_bytes - wscan;
   hipStream_t st = (hipStream_t)stream;
-  // Validate all three parts before the first launch, so that a failure
-  // leaves every output untouched.
+  hipStream_t st2 = a->stream2 ? (hipStream_t)a->stream2 : st;
+  HM_REQUIRE(st2 != st || a->stream2 == nullptr, HM_ERR_INVALID, "stream2 must differ from stream");
+  // Validate all parts before the first launch, so that a failure leaves
+  // every output untouched.
   for (int pass = 0; pass < 2; ++pass) {
-    bool dry = pass == 0;
-    hm_status s = hm::swa_meta_attn_impl(a->q, a->k, a->v, a->ya, a->B, a->T, a->Hq, a->Hkv,
-                                         a->Dh, a->n_meta, a->window, a->rope_base, a->pos0,
-                                         a->scale, a->dtype, ws, wa, st, dry);
+    const bool dry = pass == 0;
+    hm_status s;
+    if (!dry && st2 != st) {
+      s = hm::fork_join(st, st2, /*fork=*/true);
+      if (s != HM_OK) return s;
+    }
+    if (!a->kv_reuse) {
+      s = hm::attn_kv_prepare_impl(a->k, a->v, kv, kvb, a->B, a->T, a->Hkv, a->Dh, a->rope_base,
+                                   a->pos0, a->dtype, st, dry);
+      if (s != HM_OK) return s;
+    }
+    s = hm::attn_with_kv_impl(a->q, kv, kvb, a->ya, a->B, a->T, a->Hq, a->Hkv, a->Dh, a->n_meta,
+                              a->window, a->rope_base, a->pos0, a->scale, a->dtype, st, dry);
     if (s != HM_OK) return s;
     s = hm::conv_scan_impl(a->x, a->conv_w, a->conv_b, nullptr, a->conv_state_out, a->delta,
                            a->A, a->Bm, a->Cm, a->D, a->z, nullptr, a->ys, a->h_out, a->B,
-                           a->T, a->Di, a->K, a->N, a->dtype, ws + wa, a->workspace_bytes - wa,
-                           st, /*fuse_conv=*/true, dry);
+                           a->T, a->Di, a->K, a->N, a->dtype, ws, wscan, st2,
+                           /*fuse_conv=*/true, dry);
     if (s != HM_OK) return s;
+    if (!dry && st2 != st) {
+      s = hm::fork_join(st, st2, /*fork=*/false);
+      if (s != HM_OK) return s;
+    }
     s = hm::norm_mean_impl(a->ya, a->ys, a->beta_a, a->beta_s, a->eps, a->out,
                            (long long)a->B * a->T, a->Di, a->dtype, st, dry);
     if (s != HM_OK) return s;

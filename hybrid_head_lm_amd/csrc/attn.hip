@@ -36,6 +36,13 @@ constexpr int kBM = 128;     // query rows per workgroup
 constexpr int kWR = 32;      // query rows per wave
 constexpr int kBN = 64;      // keys per tile
 constexpr int kLdsRow = 72;  // padded LDS row (bf16 elements): 144 B keeps 16-B reads conflict-free
+constexpr int kStages = 4;   // K/V tiles in flight per workgroup (LDS ring)
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] |
+// vmcnt[5:4] in bits 15:14): wait until at most N vector-memory ops are
+// outstanding, leave the other counters unconstrained.
+constexpr int kVmcnt8 = vmcnt_imm(8);
+constexpr int kVmcnt4 = vmcnt_imm(4);
+constexpr int kVmcnt0 = vmcnt_imm(0);
 
 // Swap bits 2 and 3 of a row index inside a 32-row block.  K rows are stored in
 // LDS in this order so that the 32x32 MFMA output gives each lane half 8
@@ -96,12 +103,30 @@ __global__ __launch_bounds__(256) void attn_prep_bf16(
 }
 
 // ---------------------------------------------------------------- bf16 flash kernel
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
+// LDS tiles (K and V^T alike): 64 rows of 128 bytes; the 16-byte chunk c of
+// row r lives in slot c ^ (r & 7), so the 8 lanes that read chunk c of 8
+// consecutive rows hit 8 different bank groups.  LDS row r of the K tile holds
+// key swap_b23(r).  Tiles go HBM -> LDS with global_load_lds_dwordx4 (no
+// register staging), double buffered, one barrier per tile.
+HM_DEV int lds_off(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+
+// sin/cos of pos * theta with the angle in double, reduced to [-1/2, 1/2]
+// revolutions; hardware v_sin/v_cos (plenty for bf16 operands).
+HM_DEV void rot_rev(long long pos, double theta, float* s, float* c) {
+  const double inv2pi = 0.15915494309189533576888376337251;
+  double r = (double)pos * theta * inv2pi;
+  r -= rint(r);
+  *s = __builtin_amdgcn_sinf((float)r);
+  *c = __builtin_amdgcn_cosf((float)r);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Kr, const bf16_t* __restrict__ Vt,
     bf16_t* __restrict__ o, int T, int Tpad, int Hq, int Hkv, int M, int W, long long pos0,
     float qscale, double log2_base, int n_qt, int n_items) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][kBN * kLdsRow];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[2][64 * kLdsRow];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][8192];  // [stage][K|V^T]
 
   // Work item.  Items are ordered (b, kv group) -> query tile (heaviest
   // first) -> head within the group, and each XCD (blockIdx % 8) takes one
@@ -118,7 +143,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
   const int g = pair % Hkv, b = pair / Hkv;
   const int h = g * grp + hh;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, gq = lane >> 5;
   const int i0 = qt * kBM, i1 = min(i0 + kBM, T);
   const int wi0 = i0 + wave * kWR, wi1 = min(wi0 + kWR, T);
@@ -137,12 +163,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
 #pragma unroll
       for (int e = 0; e < 8; ++e) xs[s][e] = bf2f(p[e]);
     }
+    const double step = exp2(-log2_base / 32.0);   // theta_{d+1} / theta_d for Dh = 64
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+      double th = exp2(-(double)(16 * s + 8 * gq) / 32.0 * log2_base);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float sn, cs;
-        rope_sincos(pos0 + qrow, 16 * s + 8 * gq + e, 64, log2_base, &sn, &cs);
+        rot_rev(pos0 + qrow, th, &sn, &cs);
+        th *= step;
         const float x1 = xs[s][e], x2 = xs[s + 2][e];
         xs[s][e] = (x1 * cs - x2 * sn) * qscale;
         xs[s + 2][e] = (x2 * cs + x1 * sn) * qscale;
@@ -158,99 +187,136 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
   const int nt0 = rg.e0;
   const int ntiles = nt0 + (rg.e1 - rg.b1);
 
-  const bf16_t* Kbase = Kr + (size_t)pair * Tpad * 64;
-  const bf16_t* Vbase = Vt + (size_t)pair * (Tpad / 64) * 4096;
-
-  uint4 rk[2], rv[2];
-  auto gload = [&](int tile) {
-    const bf16_t* kp = Kbase + (size_t)tile * 4096;
-    const bf16_t* vp = Vbase + (size_t)tile * 4096;
+  const unsigned char* Kbase = (const unsigned char*)(Kr + (size_t)pair * Tpad * 64);
+  const unsigned char* Vbase = (const unsigned char*)(Vt + (size_t)pair * (Tpad / 64) * 4096);
+  // This thread's two 16-byte chunks of each tile: LDS rows 16*wave + 8*i + lane/8,
+  // slot lane & 7 (global_load_lds writes lane L of a wave at base + 16 L).
+  int koff[2], voff[2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int c = threadIdx.x + 256 * r;
-      rk[r] = *(const uint4*)(kp + c * 8);
-      rv[r] = *(const uint4*)(vp + c * 8);
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * wave + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ (r & 7);
+    koff[i] = swap_b23(r) * 128 + c * 16;
+    voff[i] = r * 128 + c * 16;
+  }
+  auto issue = [&](int tile, int buf) {
+    const unsigned char* kp = Kbase + (size_t)tile * 8192;
+    const unsigned char* vp = Vbase + (size_t)tile * 8192;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_global_load_lds((const void*)(kp + koff[i]),
+                                       (lds_void*)&smem[buf][0][(16 * wave + 8 * i) * 128], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vp + voff[i]),
+                                       (lds_void*)&smem[buf][1][(16 * wave + 8 * i) * 128], 16, 0, 0);
     }
   };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int c = threadIdx.x + 256 * r;
-      const int row = c >> 3, col = c & 7;
-      *(uint4*)(&sK[buf][swap_b23(row) * kLdsRow + col * 8]) = rk[r];
-      *(uint4*)(&sV[buf][row * kLdsRow + col * 8]) = rv[r];
-    }
-  };
+  auto tile_at = [&](int it) { return it < nt0 ? it : rg.b1 + (it - nt0); };
 
-  f32x16_v acc[2];
+  // Online softmax in log2 units with a lazily moved reference m_ref: the
+  // MFMA accumulates onto -m_ref, so it yields S - m_ref directly; m_ref moves
+  // (and O, l are rescaled) only when a tile's maximum exceeds it by > 8.
+  f32x16_v acc[2], cinit;
 #pragma unroll
-  for (int db = 0; db < 2; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-  float m_run = -1e30f, l_run = 0.f;
+  for (int i = 0; i < 16; ++i) {
+    acc[0][i] = 0.f;
+    acc[1][i] = 0.f;
+    cinit[i] = 0.f;
+  }
+  float m_ref = 0.f, l_run = 0.f;
+  bool fresh = true;
   const float NEG_INF = -__builtin_huge_valf();
 
-  if (ntiles > 0) gload(0 < nt0 ? 0 : rg.b1);
+  // LDS ring of kStages = 4 tiles: tile t is issued three iterations before
+  // it is used, into the stage that tile t-4 released.  At the top of
+  // iteration `it` the thread waits until its own loads of tile `it` have
+  // landed (4 loads per thread per tile; the tiles after it may stay in
+  // flight), and the barrier publishes the tile to every wave and frees the
+  // stage of tile it-1 for tile it+3.
+  static_assert(kStages == 4, "the wait counts below assume a 4-stage ring");
+#pragma unroll
+  for (int p = 0; p < kStages - 1; ++p)
+    if (p < ntiles) issue(tile_at(p), p);
+
   for (int it = 0; it < ntiles; ++it) {
-    const int tile = it < nt0 ? it : rg.b1 + (it - nt0);
-    const int buf = it & 1;
-    swrite(buf);
+    const int after = min(2, ntiles - 1 - it);
+    if (after == 2) __builtin_amdgcn_s_waitcnt(kVmcnt8);
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(kVmcnt4);
+    else __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    if (it + 1 < ntiles) gload(it + 1 < nt0 ? it + 1 : rg.b1 + (it + 1 - nt0));
-    const int j0 = tile * kBN;
+    if (it + 3 < ntiles) issue(tile_at(it + 3), (it + 3) % kStages);
+    const int j0 = tile_at(it) * kBN;
     const int cls = hm_tile_class(wi0, wi1, j0, min(j0 + kBN, T), M, W);
-    if (cls != 0) {
-      f32x16_v S[2];
+    if (cls == 0) continue;
+    // S^T - m_ref (accumulated onto -m_ref); the two 32-key blocks are
+    // independent accumulation chains, alternated
+    const unsigned char* sk = smem[it % kStages][0];
+    f32x16_v S[2];
+    S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_v*)(sk + lds_off(n, gq)),
+                                                   qf[0], cinit, 0, 0, 0);
+    S[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_v*)(sk + lds_off(32 + n, gq)),
+                                                   qf[0], cinit, 0, 0, 0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int s = 1; s < 4; ++s)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) S[kb][i] = 0.f;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8_v a = *(const bf16x8_v*)(&sK[buf][(kb * 32 + n) * kLdsRow + 16 * s + 8 * gq]);
-          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], S[kb], 0, 0, 0);
-        }
-      }
-      if (cls == 1 || j0 + kBN > T) {
-        const int qi = wi0 + n;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = j0 + 32 * kb + 16 * (i >> 3) + 8 * gq + (i & 7);
-            if (!hm_visible(qi, key, M, W)) S[kb][i] = NEG_INF;
-          }
-      }
-      float mx = S[0][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, S[0][i]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[1][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      float ls = 0.f;
-      bf16x8_v pf[4];
+      for (int kb = 0; kb < 2; ++kb)
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const bf16x8_v*)(sk + lds_off(kb * 32 + n, 2 * s + gq)), qf[s], S[kb], 0, 0, 0);
+    if (cls == 1 || j0 + kBN > T) {
+      const int qi = wi0 + n;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(S[kb][i] - m_new);
-          ls += p;
-          pf[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
+          const int key = j0 + 32 * kb + 16 * (i >> 3) + 8 * gq + (i & 7);
+          if (!hm_visible(qi, key, M, W)) S[kb][i] = NEG_INF;
         }
-      l_run = l_run * alpha + ls;
+    }
+    float mx = fmaxf(S[0][0], S[0][1]);
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
+    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, S[0][i]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[1][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool need = fresh ? (mx > NEG_INF) : (mx > 8.f);
+    if (__ballot(need) != 0) {
+      // move the reference: rescale O and l and shift this tile's scores
+      const float delta = need ? mx : 0.f;
+      const float alpha = fresh ? 0.f : fast_exp2(-delta);
+      if (need) fresh = false;
+      m_ref += delta;
+      l_run *= alpha;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8_v a = *(const bf16x8_v*)(&sV[buf][(db * 32 + n) * kLdsRow + 16 * s + 8 * gq]);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s], acc[db], 0, 0, 0);
-        }
+      for (int i = 0; i < 16; ++i) {
+        acc[0][i] *= alpha;
+        acc[1][i] *= alpha;
+        S[0][i] -= delta;
+        S[1][i] -= delta;
+        cinit[i] = -m_ref;
       }
+    }
+    bf16x8_v pf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pf[2 * kb + (i >> 3)][i & 7] = (__bf16)fast_exp2(S[kb][i]);
+    // row sums of the bf16 probabilities actually used by the PV product
+    typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+    const bf16x2_v ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2_v pr = {pf[s][2 * e], pf[s][2 * e + 1]};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+      }
+    const unsigned char* sv = smem[it % kStages][1];
+#pragma unroll
+    for (int db = 0; db < 2; ++db) {
+      const int row = db * 32 + n;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const bf16x8_v*)(sv + lds_off(row, 2 * s + gq)), pf[s], acc[db], 0, 0, 0);
     }
   }
 
@@ -275,7 +341,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
 // ---------------------------------------------------------------- float32 path
 template <int DH>
 __global__ __launch_bounds__(256) void attn_prep_f32(const float* __restrict__ k,
-                                                     float* __restrict__ Kr, int B, int T,
+                                                     const float* __restrict__ v,
+                                                     float* __restrict__ Kr,
+                                                     float* __restrict__ Vc, int B, int T,
                                                      int Hkv, long long pos0, double log2_base) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)B * T * Hkv * (DH / 2);
@@ -284,13 +352,15 @@ __global__ __launch_bounds__(256) void attn_prep_f32(const float* __restrict__ k
   const int g = (idx / (DH / 2)) % Hkv;
   const int t = (idx / ((DH / 2) * Hkv)) % T;
   const int b = idx / ((long long)(DH / 2) * Hkv * T);
-  const float* src = k + (((size_t)b * T + t) * Hkv + g) * DH;
+  const size_t row = (((size_t)b * T + t) * Hkv + g) * DH;
   float sn, cs;
   rope_sincos(pos0 + t, d, DH, log2_base, &sn, &cs);
-  const float x1 = src[d], x2 = src[d + DH / 2];
+  const float x1 = k[row + d], x2 = k[row + d + DH / 2];
   float* dst = Kr + (((size_t)b * Hkv + g) * T + t) * DH;
   dst[d] = x1 * cs - x2 * sn;
   dst[d + DH / 2] = x2 * cs + x1 * sn;
+  Vc[row + d] = v[row + d];
+  Vc[row + d + DH / 2] = v[row + d + DH / 2];
 }
 
 template <int DH>
@@ -350,7 +420,7 @@ __global__ __launch_bounds__(128) void attn_fwd_f32(const float* __restrict__ q,
 __global__ void debug_mask_kernel(int T, int M, int W, unsigned char* out) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long long)T * T) return;
-  out[idx] = hm_visible(idx / T, idx % T, M, W) ? 1 : 0;
+  out[idx] = hm_visible((int)(idx / T), (int)(idx % T), M, W) ? 1 : 0;
 }
 
 __global__ void debug_tile_kernel(int T, int M, int W, int bm, int bn, int* out) {
@@ -372,85 +442,170 @@ __global__ void debug_tile_kernel(int T, int M, int W, int bm, int bn, int* out)
 
 namespace hm {
 
-hm_status swa_meta_attn_impl(const void* q, const void* k, const void* v, void* o, int B,
-                             int T, int Hq, int Hkv, int Dh, int n_meta, int window,
-                             float rope_base, long long pos0, float scale, hm_dtype dtype,
-                             void* workspace, size_t workspace_bytes, hipStream_t st,
-                             bool dry) {
-  HM_PTR(q);
-  HM_PTR(k);
-  HM_PTR(v);
-  HM_PTR(o);
-  HM_REQUIRE(B > 0 && T > 0 && Hq > 0 && Hkv > 0 && Dh > 0, HM_ERR_INVALID,
-             "B, T, Hq, Hkv and Dh must be positive");
-  HM_REQUIRE(Hq % Hkv == 0, HM_ERR_INVALID, "Hq must be a multiple of Hkv");
-  HM_REQUIRE(n_meta >= 0 && n_meta <= T, HM_ERR_INVALID, "need 0 <= n_meta <= T");
+// Shapes and options shared by the prepare and attend halves.
+static hm_status attn_check(int B, int T, int Hkv, int Dh, float rope_base, long long pos0,
+                            hm_dtype dtype) {
+  HM_REQUIRE(B > 0 && T > 0 && Hkv > 0 && Dh > 0, HM_ERR_INVALID,
+             "B, T, Hkv and Dh must be positive");
   HM_REQUIRE(pos0 >= 0, HM_ERR_INVALID, "pos0 must be >= 0");
   HM_REQUIRE(rope_base > 1.0f && std::isfinite(rope_base), HM_ERR_INVALID, "rope_base must be > 1");
-  HM_REQUIRE(std::isfinite(scale), HM_ERR_INVALID, "scale must be finite");
-  HM_REQUIRE(o != q && o != k && o != v, HM_ERR_INVALID, "o must not alias an input");
   HM_REQUIRE(dtype == HM_BF16 || dtype == HM_F32, HM_ERR_UNSUPPORTED, "dtype must be f32 or bf16");
   if (dtype == HM_BF16)
     HM_REQUIRE(Dh == 64, HM_ERR_UNSUPPORTED, "bf16 attention supports Dh = 64 only");
   else
     HM_REQUIRE(Dh == 16 || Dh == 32 || Dh == 64, HM_ERR_UNSUPPORTED,
                "f32 attention supports Dh in {16, 32, 64}");
-  HM_REQUIRE((double)B * T * Hq * Dh < 4.0e9 && B <= 65535 && Hkv <= 65535, HM_ERR_UNSUPPORTED,
-             "tensor too large");
-  const size_t need = hm_swa_meta_attn_workspace(B, T, Hkv, Dh, dtype);
-  HM_REQUIRE(workspace != nullptr && workspace_bytes >= need && aligned16(workspace),
-             HM_ERR_WORKSPACE, "workspace smaller than hm_swa_meta_attn_workspace()");
-  if (dry) return HM_OK;
+  HM_REQUIRE(B <= 65535 && Hkv <= 65535 && T <= (1 << 24), HM_ERR_UNSUPPORTED, "tensor too large");
+  return HM_OK;
+}
 
+hm_status attn_kv_prepare_impl(const void* k, const void* v, void* kv, size_t kv_bytes, int B,
+                               int T, int Hkv, int Dh, float rope_base, long long pos0,
+                               hm_dtype dtype, hipStream_t st, bool dry) {
+  HM_PTR(k);
+  HM_PTR(v);
+  HM_PTR(kv);
+  hm_status s = attn_check(B, T, Hkv, Dh, rope_base, pos0, dtype);
+  if (s != HM_OK) return s;
+  HM_REQUIRE((double)B * T * Hkv * Dh < 4.0e9, HM_ERR_UNSUPPORTED, "tensor too large");
+  HM_REQUIRE(kv_bytes >= hm_attn_kv_bytes(B, T, Hkv, Dh, dtype), HM_ERR_WORKSPACE,
+             "kv buffer smaller than hm_attn_kv_bytes()");
+  HM_REQUIRE(kv != k && kv != v, HM_ERR_INVALID, "kv must not alias k or v");
+  if (dry) return HM_OK;
+  const double l2b = log2((double)rope_base);
+  if (dtype == HM_BF16) {
+    const int Tpad = (T + 63) / 64 * 64;
+    bf16_t* Kr = (bf16_t*)kv;
+    bf16_t* Vt = Kr + (size_t)B * Hkv * Tpad * 64;
+    hipLaunchKernelGGL(attn_prep_bf16, dim3(Tpad / 64, Hkv, B), dim3(256), 0, st,
+                       (const bf16_t*)k, (const bf16_t*)v, Kr, Vt, T, Tpad, Hkv, pos0, l2b);
+    return check_launch("attn_prep_bf16");
+  }
+  float* Kr = (float*)kv;
+  float* Vc = Kr + (size_t)B * Hkv * T * Dh;
+  const long long np = (long long)B * T * Hkv * (Dh / 2);
+  const dim3 grid((unsigned)((np + 255) / 256));
+  switch (Dh) {
+    case 16:
+      hipLaunchKernelGGL(attn_prep_f32<16>, grid, dim3(256), 0, st, (const float*)k,
+                         (const float*)v, Kr, Vc, B, T, Hkv, pos0, l2b);
+      break;
+    case 32:
+      hipLaunchKernelGGL(attn_prep_f32<32>, grid, dim3(256), 0, st, (const float*)k,
+                         (const float*)v, Kr, Vc, B, T, Hkv, pos0, l2b);
+      break;
+    default:
+      hipLaunchKernelGGL(attn_prep_f32<64>, grid, dim3(256), 0, st, (const float*)k,
+                         (const float*)v, Kr, Vc, B, T, Hkv, pos0, l2b);
+      break;
+  }
+  return check_launch("attn_prep_f32");
+}
+
+hm_status attn_with_kv_impl(const void* q, const void* kv, size_t kv_bytes, void* o, int B,
+                            int T, int Hq, int Hkv, int Dh, int n_meta, int window,
+                            float rope_base, long long pos0, float scale, hm_dtype dtype,
+                            hipStream_t st, bool dry) {
+  HM_PTR(q);
+  HM_PTR(kv);
+  HM_PTR(o);
+  hm_status s = attn_check(B, T, Hkv, Dh, rope_base, pos0, dtype);
+  if (s != HM_OK) return s;
+  HM_REQUIRE(Hq > 0 && Hq % Hkv == 0, HM_ERR_INVALID, "Hq must be a positive multiple of Hkv");
+  HM_REQUIRE(n_meta >= 0 && n_meta <= T, HM_ERR_INVALID, "need 0 <= n_meta <= T");
+  HM_REQUIRE(std::isfinite(scale), HM_ERR_INVALID, "scale must be finite");
+  HM_REQUIRE(o != q && o != kv, HM_ERR_INVALID, "o must not alias q or kv");
+  HM_REQUIRE((double)B * T * Hq * Dh < 4.0e9 && (double)B * Hq * ((T + kBM - 1) / kBM) < 2.0e9,
+             HM_ERR_UNSUPPORTED, "tensor too large");
+  HM_REQUIRE(kv_bytes >= hm_attn_kv_bytes(B, T, Hkv, Dh, dtype), HM_ERR_WORKSPACE,
+             "kv buffer smaller than hm_attn_kv_bytes()");
+  if (dry) return HM_OK;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)Dh);
   const double l2b = log2((double)rope_base);
   if (dtype == HM_BF16) {
     const int Tpad = (T + 63) / 64 * 64;
-    bf16_t* Kr = (bf16_t*)workspace;
-    bf16_t* Vt = Kr + (size_t)B * Hkv * Tpad * 64;
-    hipLaunchKernelGGL(attn_prep_bf16, dim3(Tpad / 64, Hkv, B), dim3(256), 0, st,
-                       (const bf16_t*)k, (const bf16_t*)v, Kr, Vt, T, Tpad, Hkv, pos0, l2b);
-    hm_status s = check_launch("attn_prep_bf16");
-    if (s != HM_OK) return s;
+    const bf16_t* Kr = (const bf16_t*)kv;
+    const bf16_t* Vt = Kr + (size_t)B * Hkv * Tpad * 64;
     const int n_qt = (T + kBM - 1) / kBM;
     const int n_items = B * Hq * n_qt;
     const int grid = (n_items + 7) / 8 * 8;
-    hipLaunchKernelGGL(attn_fwd_bf16, dim3(grid), dim3(256), 0, st, (const bf16_t*)q,
-                       (const bf16_t*)Kr, (const bf16_t*)Vt, (bf16_t*)o, T, Tpad, Hq, Hkv,
-                       n_meta, window, pos0, sc * kLog2e, l2b, n_qt, n_items);
+    hipLaunchKernelGGL(attn_fwd_bf16, dim3(grid), dim3(256), 0, st, (const bf16_t*)q, Kr, Vt,
+                       (bf16_t*)o, T, Tpad, Hq, Hkv, n_meta, window, pos0, sc * kLog2e, l2b, n_qt,
+                       n_items);
     return check_launch("attn_fwd_bf16");
   }
-  float* Kr = (float*)workspace;
-  const long long np = (long long)B * T * Hkv * (Dh / 2);
+  const float* Kr = (const float*)kv;
+  const float* Vc = Kr + (size_t)B * Hkv * T * Dh;
   const long long nq = (long long)B * Hq * T;
-#define HM_F32_CASE(DHV)                                                                    \
-  case DHV:                                                                                 \
-    hipLaunchKernelGGL(attn_prep_f32<DHV>, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, \
-                       st, (const float*)k, Kr, B, T, Hkv, pos0, l2b);                       \
-    hipLaunchKernelGGL(attn_fwd_f32<DHV>, dim3((unsigned)((nq + 127) / 128)), dim3(128), 0, \
-                       st, (const float*)q, (const float*)Kr, (const float*)v, (float*)o, B, \
-                       T, Hq, Hkv, n_meta, window, pos0, sc, l2b);                           \
-    break;
+  const dim3 grid((unsigned)((nq + 127) / 128));
   switch (Dh) {
-    HM_F32_CASE(16)
-    HM_F32_CASE(32)
-    HM_F32_CASE(64)
+    case 16:
+      hipLaunchKernelGGL(attn_fwd_f32<16>, grid, dim3(128), 0, st, (const float*)q, Kr, Vc,
+                         (float*)o, B, T, Hq, Hkv, n_meta, window, pos0, sc, l2b);
+      break;
+    case 32:
+      hipLaunchKernelGGL(attn_fwd_f32<32>, grid, dim3(128), 0, st, (const float*)q, Kr, Vc,
+                         (float*)o, B, T, Hq, Hkv, n_meta, window, pos0, sc, l2b);
+      break;
+    default:
+      hipLaunchKernelGGL(attn_fwd_f32<64>, grid, dim3(128), 0, st, (const float*)q, Kr, Vc,
+                         (float*)o, B, T, Hq, Hkv, n_meta, window, pos0, sc, l2b);
+      break;
   }
-#undef HM_F32_CASE
   return check_launch("attn_fwd_f32");
+}
+
+hm_status swa_meta_attn_impl(const void* q, const void* k, const void* v, void* o, int B,
+                             int T, int Hq, int Hkv, int Dh, int n_meta, int window,
+                             float rope_base, long long pos0, float scale, hm_dtype dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t st,
+                             bool dry) {
+  HM_REQUIRE(o != k && o != v, HM_ERR_INVALID, "o must not alias k or v");
+  HM_REQUIRE(workspace != nullptr && aligned16(workspace), HM_ERR_WORKSPACE,
+             "workspace must be a non-NULL 16-byte aligned buffer");
+  // validate both halves before launching either
+  hm_status s = attn_kv_prepare_impl(k, v, workspace, workspace_bytes, B, T, Hkv, Dh, rope_base,
+                                     pos0, dtype, st, true);
+  if (s != HM_OK) return s;
+  s = attn_with_kv_impl(q, workspace, workspace_bytes, o, B, T, Hq, Hkv, Dh, n_meta, window,
+                        rope_base, pos0, scale, dtype, st, true);
+  if (s != HM_OK || dry) return s;
+  s = attn_kv_prepare_impl(k, v, workspace, workspace_bytes, B, T, Hkv, Dh, rope_base, pos0, dtype,
+                           st, false);
+  if (s != HM_OK) return s;
+  return attn_with_kv_impl(q, workspace, workspace_bytes, o, B, T, Hq, Hkv, Dh, n_meta, window,
+                           rope_base, pos0, scale, dtype, st, false);
 }
 
 }  // namespace hm
 
 extern "C" {
 
-size_t hm_swa_meta_attn_workspace(int B, int T, int Hkv, int Dh, hm_dtype dtype) {
+size_t hm_attn_kv_bytes(int B, int T, int Hkv, int Dh, hm_dtype dtype) {
   if (B <= 0 || T <= 0 || Hkv <= 0 || Dh <= 0) return 0;
   if (dtype == HM_BF16) {
     const size_t Tpad = (size_t)(T + 63) / 64 * 64;
     return 2 * (size_t)B * Hkv * Tpad * 64 * sizeof(bf16_t);
   }
-  return (size_t)B * Hkv * T * Dh * sizeof(float);
+  return 2 * (size_t)B * Hkv * T * Dh * sizeof(float);
+}
+
+size_t hm_swa_meta_attn_workspace(int B, int T, int Hkv, int Dh, hm_dtype dtype) {
+  return hm_attn_kv_bytes(B, T, Hkv, Dh, dtype);
+}
+
+hm_status hm_attn_kv_prepare(const void* k, const void* v, void* kv, size_t kv_bytes, int B,
+                             int T, int Hkv, int Dh, float rope_base, long long pos0,
+                             hm_dtype dtype, void* stream) {
+  return hm::attn_kv_prepare_impl(k, v, kv, kv_bytes, B, T, Hkv, Dh, rope_base, pos0, dtype,
+                                  (hipStream_t)stream, false);
+}
+
+hm_status hm_attn_with_kv(const void* q, const void* kv, size_t kv_bytes, void* o, int B, int T,
+                          int Hq, int Hkv, int Dh, int n_meta, int window, float rope_base,
+                          long long pos0, float scale, hm_dtype dtype, void* stream) {
+  return hm::attn_with_kv_impl(q, kv, kv_bytes, o, B, T, Hq, Hkv, Dh, n_meta, window, rope_base,
+                               pos0, scale, dtype, (hipStream_t)stream, false);
 }
 
 hm_status hm_swa_meta_attn(const void* q, const void* k, const void* v, void* o, int B, int T,

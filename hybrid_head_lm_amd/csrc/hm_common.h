@@ -47,11 +47,17 @@ template <> struct ActIO<bf16_t> {
   static HM_DEV void st(bf16_t* p, float v) { *p = f2bf(v); }
 };
 
-HM_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-HM_DEV float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
-HM_DEV float siluf_(float x) { return x / (1.0f + __expf(-x)); }
-
 constexpr float kLog2e = 1.4426950408889634f;
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector memory
+// operations are outstanding and leaves the other counters unconstrained.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+HM_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// SiLU(x) = x * sigmoid(x) with hardware exp2 and reciprocal (about 1 ulp each).
+HM_DEV float siluf_(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
 
 // RoPE angle for position `pos` and frequency index d of head dim Dh, reduced
 // to [-pi, pi] in double precision, then sin/cos in float.
@@ -64,7 +70,7 @@ HM_DEV void rope_sincos(long long pos, int d, int Dh, double log2_base, float* s
 }
 
 // ----------------------------------------------------------------- visibility
-HM_HD bool hm_visible(long long i, long long j, int M, int W) {
+HM_HD bool hm_visible(int i, int j, int M, int W) {
   if (j > i) return false;
   if (j < M || W <= 0) return true;
   return i - j < W;
@@ -112,6 +118,7 @@ namespace hm {
 void set_error(const std::string& msg);
 hm_status fail(hm_status s, const std::string& msg);
 hm_status check_launch(const char* what);
+hm_status fork_join(hipStream_t main, hipStream_t side, bool fork);
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -127,6 +134,13 @@ hm_status swa_meta_attn_impl(const void* q, const void* k, const void* v, void* 
                              float rope_base, long long pos0, float scale, hm_dtype dtype,
                              void* workspace, size_t workspace_bytes, hipStream_t st,
                              bool dry);
+hm_status attn_kv_prepare_impl(const void* k, const void* v, void* kv, size_t kv_bytes, int B,
+                               int T, int Hkv, int Dh, float rope_base, long long pos0,
+                               hm_dtype dtype, hipStream_t st, bool dry);
+hm_status attn_with_kv_impl(const void* q, const void* kv, size_t kv_bytes, void* o, int B,
+                            int T, int Hq, int Hkv, int Dh, int n_meta, int window,
+                            float rope_base, long long pos0, float scale, hm_dtype dtype,
+                            hipStream_t st, bool dry);
 hm_status conv_scan_impl(const void* x, const float* conv_w, const float* conv_b,
                          const float* conv_state_in, float* conv_state_out,
                          const void* delta, const float* A, const void* Bm, const void* Cm,

@@ -54,7 +54,11 @@ struct Vec8<float> {  // 8 floats = two 16-byte accesses
   }
 };
 
-// width % 8 == 0 (16-byte aligned rows)
+// width % 8 == 0 (16-byte aligned rows).  Rows of up to 64 * 8 * MAXC
+// elements stay in registers between the two passes (one HBM read per row);
+// wider rows are read twice (the second read is served by L2).
+constexpr int kMaxC = 4;
+
 template <typename Tact>
 __global__ __launch_bounds__(256) void norm_mean_vec(const Tact* __restrict__ ya,
                                                      const Tact* __restrict__ ys,
@@ -67,8 +71,47 @@ __global__ __launch_bounds__(256) void norm_mean_vec(const Tact* __restrict__ ya
   const int lane = threadIdx.x & 63;
   const Tact* pa = ya + row * width;
   const Tact* ps = ys + row * width;
+  Tact* po = out + row * width;
   const int n8 = width >> 3;
   float sa = 0.f, ss = 0.f;
+  if (n8 <= 64 * kMaxC) {
+    float a[kMaxC][8], s[kMaxC][8];
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k) {
+      const int c = lane + 64 * k;
+      if (c < n8) {
+        Vec8<Tact>::ld(pa + 8 * c, a[k]);
+        Vec8<Tact>::ld(ps + 8 * c, s[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k)
+      if (lane + 64 * k < n8)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          sa += a[k][i] * a[k][i];
+          ss += s[k][i] * s[k][i];
+        }
+    sa = wave_sum(sa);
+    ss = wave_sum(ss);
+    const float ra = 0.5f / sqrtf(sa / (float)width + eps);
+    const float rs = 0.5f / sqrtf(ss / (float)width + eps);
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k) {
+      const int c = lane + 64 * k;
+      if (c < n8) {
+        const float4 ba0 = *(const float4*)(ba + 8 * c), ba1 = *(const float4*)(ba + 8 * c + 4);
+        const float4 bs0 = *(const float4*)(bs + 8 * c), bs1 = *(const float4*)(bs + 8 * c + 4);
+        const float wa[8] = {ba0.x, ba0.y, ba0.z, ba0.w, ba1.x, ba1.y, ba1.z, ba1.w};
+        const float wsv[8] = {bs0.x, bs0.y, bs0.z, bs0.w, bs1.x, bs1.y, bs1.z, bs1.w};
+        float r[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = wa[i] * a[k][i] * ra + wsv[i] * s[k][i] * rs;
+        Vec8<Tact>::st(po + 8 * c, r);
+      }
+    }
+    return;
+  }
   for (int c = lane; c < n8; c += 64) {
     float a[8], s[8];
     Vec8<Tact>::ld(pa + 8 * c, a);
@@ -83,7 +126,6 @@ __global__ __launch_bounds__(256) void norm_mean_vec(const Tact* __restrict__ ya
   ss = wave_sum(ss);
   const float ra = 0.5f / sqrtf(sa / (float)width + eps);
   const float rs = 0.5f / sqrtf(ss / (float)width + eps);
-  Tact* po = out + row * width;
   for (int c = lane; c < n8; c += 64) {
     float a[8], s[8], r[8];
     Vec8<Tact>::ld(pa + 8 * c, a);

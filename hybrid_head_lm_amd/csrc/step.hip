@@ -10,22 +10,23 @@
 // With one n_prev for the batch the visible rows are exactly the contiguous
 // range [0, M + min(n_prev+1, W)).
 //
-// Three launches per layer:
-//   step_ssm_kv      conv step + one scan step per (b, channel), in place on the
-//                    states, branch output to the workspace; the producer layer's
-//                    extra blocks rotate k_new and write k_new / v_new into the
-//                    token's slot (so the next launch sees them);
-//   step_attn_bf16   split over keys: a workgroup of 4 waves covers 256 cache
-//                    rows of one (b, kv group); each wave takes 64 rows, computes
-//                    S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (the group's query
-//                    heads on the 16 MFMA columns, K straight from HBM as the A
-//                    operand), a softmax, and O^T = V^T P^T with V^T staged
-//                    through LDS; the 4 waves merge in LDS and write one partial
-//                    (max, sum, unnormalised O) per head;
-//   step_combine     per sequence: merge the partials into Y_attn, then the
-//                    branch RMS norm, rescale and average with Y_ssm.
-// A float32 path (any Dh in {16, 32, 64}) replaces the split kernel with one
-// thread per (b, head) that writes a single partial.
+// bf16 path: step_fused_bf16 holds two kinds of blocks:
+//   attention blocks  split over keys: a workgroup of 4 waves covers 256 cache
+//                     rows of one (b, kv group); each wave takes 64 rows,
+//                     computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (the
+//                     group's query heads on the 16 MFMA columns, K straight
+//                     from HBM as the A operand), a softmax, and O^T = V^T P^T
+//                     with V^T staged through LDS; the 4 waves merge in LDS and
+//                     write one partial (max, sum, unnormalised O) per head.
+//                     The block whose rows hold the new token's slot (producer
+//                     layer) first rotates k_new and writes k_new / v_new there.
+//   SSM blocks        conv step + one scan step per (b, channel), in place on
+//                     the states; branch output to the workspace.
+// then step_combine (one workgroup per sequence) merges the partials into
+// Y_attn and applies the branch RMS norm, rescale and average: two launches
+// per layer.
+// float32 path (Dh in {16, 32, 64}): SSM step + KV write, one thread per
+// (b, head) over all visible rows, then the same combine kernel.
 #include <cmath>
 
 #include "hm_common.h"
@@ -39,227 +40,311 @@ constexpr int kVRow = 72;  // padded LDS row of the transposed V tile (bf16 elem
 template <typename Tact>
 HM_DEV float ldx(const Tact* p) { return ActIO<Tact>::ld(p); }
 
-// ---------------------------------------------------------------- SSM step + KV write
+// ---------------------------------------------------------------- per-sequence combine
+// One workgroup of kCombThreads per sequence b.  Part layout per sequence:
+// [Hkv][n_split][grp][Dh + 2] = (max in log2 units, sum, unnormalised O[Dh]).
+//   1) every (head, split) max / sum to LDS (one round of loads);
+//   2) per head the merge weights w[h][s] = exp2(m_s - M) / sum_s' exp2(m_s' - M) l_s';
+//   3) Y_attn[h, d] = sum_s w[h][s] O_s[h, d] (all loads of a thread issued together),
+//      then out = 0.5 (beta_a Y_attn / rms + beta_s Y_ssm / rms).
+constexpr int kCombThreads = 512;
+constexpr int kCombMaxW = 2048;      // Hq * n_split entries held in LDS
+constexpr int kCombPer = 8;          // outputs per thread (Di <= 4096)
+
 template <typename Tact>
-__global__ __launch_bounds__(256) void step_ssm_kv(
-    const Tact* __restrict__ x, const Tact* __restrict__ dl, const Tact* __restrict__ Bm,
-    const Tact* __restrict__ Cm, const Tact* __restrict__ z, const float* __restrict__ A,
-    const float* __restrict__ D, const float* __restrict__ cw, const float* __restrict__ cb,
-    float* __restrict__ conv_state, float* __restrict__ ssm_state, float* __restrict__ ys_ws,
-    int B, int Di, int n_ssm_blocks, const Tact* __restrict__ k_new,
-    const Tact* __restrict__ v_new, Tact* __restrict__ k_cache, Tact* __restrict__ v_cache,
-    int Hkv, int Dh, int S, int slot, long long pos, double log2_base) {
-  if ((int)blockIdx.x < n_ssm_blocks) {
-    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (long long)B * Di) return;
-    const int c = idx % Di;
-    const int b = idx / Di;
-    float* cs = conv_state + idx * 3;
-    const float s0 = cs[0], s1 = cs[1], s2 = cs[2];
-    const float xv = ldx(x + idx);
-    const float u = cb[c] + cw[c * 4 + 0] * s0 + cw[c * 4 + 1] * s1 + cw[c * 4 + 2] * s2 +
-                    cw[c * 4 + 3] * xv;
-    cs[0] = s1;
-    cs[1] = s2;
-    cs[2] = xv;
-    const float xc = siluf_(u);
-    const float dv = ldx(dl + idx);
-    const float du = dv * xc;
-    float* hs = ssm_state + idx * kNS;
-    const float4* h4 = (const float4*)hs;
-    float h[kNS];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 t = h4[i];
-      h[4 * i] = t.x; h[4 * i + 1] = t.y; h[4 * i + 2] = t.z; h[4 * i + 3] = t.w;
-    }
-    const Tact* Bb = Bm + (size_t)b * kNS;
-    const Tact* Cb = Cm + (size_t)b * kNS;
-    float yv = 0.f;
-#pragma unroll
-    for (int nn = 0; nn < kNS; ++nn) {
-      h[nn] = fast_exp2(dv * (A[c * kNS + nn] * kLog2e)) * h[nn] + du * ldx(Bb + nn);
-      yv += ldx(Cb + nn) * h[nn];
-    }
-    float4* o4 = (float4*)hs;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      o4[i] = make_float4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
-    yv += D[c] * xc;
-    yv *= siluf_(ldx(z + idx));
-    ys_ws[idx] = yv;
-    return;
+__global__ __launch_bounds__(kCombThreads) void step_combine(
+    const float* __restrict__ part, size_t part_b_stride, const float* __restrict__ ys_ws,
+    size_t ys_stride, const float* __restrict__ ba, const float* __restrict__ bs, float eps,
+    Tact* __restrict__ out, float* __restrict__ ya_out, float* __restrict__ ys_out, int Hq,
+    int Hkv, int Dh, int n_split, int Di) {
+  __shared__ float sw[kCombMaxW];
+  __shared__ float red[2][kCombThreads / 64];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int grp = Hq / Hkv, stride = Dh + 2;
+  const float* pb = part + (size_t)b * part_b_stride;
+  const float* yb = ys_ws + (size_t)b * ys_stride;
+  // 1) + 2): entry e = h * n_split + s
+  for (int e = tid; e < Hq * n_split; e += kCombThreads) {
+    const int h = e / n_split, s = e % n_split;
+    const int g = h / grp, hh = h % grp;
+    sw[e] = pb[(((size_t)g * n_split + s) * grp + hh) * stride];            // max
   }
-  // producer: rotate k_new at pos and write k/v into the token's slot
-  const long long idx = (long long)(blockIdx.x - n_ssm_blocks) * 256 + threadIdx.x;
-  const int half = Dh / 2;
-  if (idx >= (long long)B * Hkv * half) return;
-  const int d = idx % half;
-  const int g = (idx / half) % Hkv;
-  const int b = idx / ((long long)half * Hkv);
-  const Tact* ks = k_new + ((size_t)b * Hkv + g) * Dh;
-  const Tact* vs = v_new + ((size_t)b * Hkv + g) * Dh;
-  float sn, cs;
-  rope_sincos(pos, d, Dh, log2_base, &sn, &cs);
-  const float x1 = ldx(ks + d), x2 = ldx(ks + d + half);
-  const size_t off = (((size_t)b * S + slot) * Hkv + g) * Dh;
-  ActIO<Tact>::st(k_cache + off + d, x1 * cs - x2 * sn);
-  ActIO<Tact>::st(k_cache + off + d + half, x2 * cs + x1 * sn);
-  v_cache[off + d] = vs[d];
-  v_cache[off + d + half] = vs[d + half];
+  __syncthreads();
+  const bool owner = tid < Hq;   // one thread per head turns maxima into weights
+  if (owner) {
+    const int h = tid, g = h / grp, hh = h % grp;
+    float M = sw[h * n_split];
+    for (int s = 1; s < n_split; ++s) M = fmaxf(M, sw[h * n_split + s]);
+    float L = 0.f;
+    for (int s = 0; s < n_split; ++s)
+      L += fast_exp2(sw[h * n_split + s] - M) * pb[(((size_t)g * n_split + s) * grp + hh) * stride + 1];
+    const float inv = 1.f / L;
+    for (int s = 0; s < n_split; ++s) sw[h * n_split + s] = fast_exp2(sw[h * n_split + s] - M) * inv;
+  }
+  __syncthreads();
+  // 3)
+  float ya[kCombPer], yv[kCombPer];
+  float sa = 0.f, ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kCombPer; ++k) {
+    const int idx = tid + k * kCombThreads;
+    ya[k] = 0.f;
+    yv[k] = 0.f;
+    if (idx < Di) {
+      const int h = idx / Dh, d = idx % Dh;
+      const int g = h / grp, hh = h % grp;
+      const float* base = pb + ((size_t)g * n_split * grp + hh) * stride + 2 + d;
+      float acc = 0.f;
+      for (int s = 0; s < n_split; ++s) acc += sw[h * n_split + s] * base[(size_t)s * grp * stride];
+      ya[k] = acc;
+      yv[k] = yb[idx];
+      sa += acc * acc;
+      ss += yv[k] * yv[k];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    sa += __shfl_xor(sa, off);
+    ss += __shfl_xor(ss, off);
+  }
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = sa;
+    red[1][tid >> 6] = ss;
+  }
+  __syncthreads();
+  sa = 0.f;
+  ss = 0.f;
+#pragma unroll
+  for (int w = 0; w < kCombThreads / 64; ++w) {
+    sa += red[0][w];
+    ss += red[1][w];
+  }
+  const float ra = 0.5f / sqrtf(sa / (float)Di + eps);
+  const float rs = 0.5f / sqrtf(ss / (float)Di + eps);
+#pragma unroll
+  for (int k = 0; k < kCombPer; ++k) {
+    const int idx = tid + k * kCombThreads;
+    if (idx < Di) {
+      ActIO<Tact>::st(out + (size_t)b * Di + idx, ba[idx] * ya[k] * ra + bs[idx] * yv[k] * rs);
+      if (ya_out) ya_out[(size_t)b * Di + idx] = ya[k];
+      if (ys_out) ys_out[(size_t)b * Di + idx] = yv[k];
+    }
+  }
 }
 
-// ---------------------------------------------------------------- bf16 split attention
-// part layout: [B*Hkv][n_split][grp][2 + 64]: max (log2 units), sum, O[64].
-__global__ __launch_bounds__(256) void step_attn_bf16(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
-    float* __restrict__ part, int Hq, int Hkv, int S, int L, long long pos, float qscale,
-    double log2_base, int n_split) {
+// ---------------------------------------------------------------- one SSM-branch step
+template <typename Tact>
+HM_DEV float ssm_step_one(int b, int c, int Di, const Tact* __restrict__ x,
+                          const Tact* __restrict__ dl, const Tact* __restrict__ Bm,
+                          const Tact* __restrict__ Cm, const Tact* __restrict__ z,
+                          const float* __restrict__ A, const float* __restrict__ D,
+                          const float* __restrict__ cw, const float* __restrict__ cb,
+                          float* __restrict__ conv_state, float* __restrict__ ssm_state) {
+  const size_t idx = (size_t)b * Di + c;
+  float* cs = conv_state + idx * 3;
+  const float s0 = cs[0], s1 = cs[1], s2 = cs[2];
+  const float xv = ldx(x + idx);
+  const float u = cb[c] + cw[c * 4 + 0] * s0 + cw[c * 4 + 1] * s1 + cw[c * 4 + 2] * s2 +
+                  cw[c * 4 + 3] * xv;
+  cs[0] = s1;
+  cs[1] = s2;
+  cs[2] = xv;
+  const float xc = siluf_(u);
+  const float dv = ldx(dl + idx);
+  const float du = dv * xc;
+  float* hs = ssm_state + idx * kNS;
+  float h[kNS];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 t = ((const float4*)hs)[i];
+    h[4 * i] = t.x; h[4 * i + 1] = t.y; h[4 * i + 2] = t.z; h[4 * i + 3] = t.w;
+  }
+  const Tact* Bb = Bm + (size_t)b * kNS;
+  const Tact* Cb = Cm + (size_t)b * kNS;
+  float y4[4] = {D[c] * xc, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int nn = 0; nn < kNS; ++nn) {
+    h[nn] = fast_exp2(dv * (A[c * kNS + nn] * kLog2e)) * h[nn] + du * ldx(Bb + nn);
+    y4[nn & 3] += ldx(Cb + nn) * h[nn];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    ((float4*)hs)[i] = make_float4(h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]);
+  return ((y4[0] + y4[1]) + (y4[2] + y4[3])) * siluf_(ldx(z + idx));
+}
+
+// ---------------------------------------------------------------- bf16 attention + SSM step
+// Blocks [0, n_attn) are (sequence, kv group, key split) attention blocks; the
+// rest are SSM-step blocks of 256 channels.  The per-sequence merge runs in the
+// next launch (step_combine), so no block depends on another.
+__global__ __launch_bounds__(256) void step_fused_bf16(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_new,
+    const bf16_t* __restrict__ v_new, bf16_t* __restrict__ kc, bf16_t* __restrict__ vc,
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ dl, const bf16_t* __restrict__ Bm,
+    const bf16_t* __restrict__ Cm, const bf16_t* __restrict__ z, const float* __restrict__ A,
+    const float* __restrict__ D, const float* __restrict__ cw, const float* __restrict__ cb,
+    float* __restrict__ conv_state, float* __restrict__ ssm_state, float* __restrict__ ys_ws, size_t ys_stride, float* __restrict__ part, size_t part_b_stride,
+    int Hq, int Hkv, int Di, int S, int L, int slot, long long pos, float qscale,
+    double log2_base, int n_split, int n_attn, int ssm_per_b) {
   __shared__ __attribute__((aligned(16))) bf16_t sVt[4][64 * kVRow];
   __shared__ float sm[4][16], sl[4][16];
   __shared__ float sO[4][16][64];
-  const int split = blockIdx.x, pair = blockIdx.y;
-  const int b = pair / Hkv, g = pair % Hkv;
+  const int tid = threadIdx.x;
   const int grp = Hq / Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, G = lane >> 4;
-
-  // Q^T fragment (B operand): lane holds head n of the group, dims 8G+e and 32+8G+e.
-  bf16x8_v qf[2];
-  if (n < grp) {
-    const bf16_t* src = q + ((size_t)b * Hq + g * grp + n) * 64;
-    const uint4 r0 = *(const uint4*)(src + 8 * G);
-    const uint4 r1 = *(const uint4*)(src + 32 + 8 * G);
-    const bf16_t* p0 = (const bf16_t*)&r0;
-    const bf16_t* p1 = (const bf16_t*)&r1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float sn, cs;
-      rope_sincos(pos, 8 * G + e, 64, log2_base, &sn, &cs);
-      const float x1 = bf2f(p0[e]), x2 = bf2f(p1[e]);
-      qf[0][e] = (__bf16)((x1 * cs - x2 * sn) * qscale);
-      qf[1][e] = (__bf16)((x2 * cs + x1 * sn) * qscale);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qf[0][e] = (__bf16)0.f;
-      qf[1][e] = (__bf16)0.f;
-    }
-  }
-
-  const int j0 = (split * 4 + wave) * 64;
-  float m_run = -1e30f, l_run = 0.f;
-  f32x4_v acc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[db][i] = 0.f;
-
-  if (j0 < L) {
+  if ((int)blockIdx.x < n_attn) {
+    const int split = blockIdx.x % n_split, pair = blockIdx.x / n_split;
+    const int b = pair / Hkv;
+    const int g = pair % Hkv;
     const size_t rs = (size_t)Hkv * 64;                   // cache row stride (elements)
-    const bf16_t* kbase = kc + ((size_t)b * S) * rs + (size_t)g * 64;
-    const bf16_t* vbase = vc + ((size_t)b * S) * rs + (size_t)g * 64;
-    // K rows in the order that gives each lane group 8 consecutive keys per
-    // 32-key step of the output.
-    bf16x8_v kf[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int key = j0 + 32 * (kb >> 1) + 8 * (n >> 2) + 4 * (kb & 1) + (n & 3);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (key < L) {
-          kf[kb][s] = *(const bf16x8_v*)(kbase + (size_t)key * rs + 32 * s + 8 * G);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kf[kb][s][e] = (__bf16)0.f;
-        }
+    if (k_new != nullptr && slot >= split * kKeysPerWG && slot < (split + 1) * kKeysPerWG) {
+      // the new token's row lies in this block's key range: write it first
+      if (tid < 32) {
+        const bf16_t* ks = k_new + ((size_t)b * Hkv + g) * 64;
+        const bf16_t* vs = v_new + ((size_t)b * Hkv + g) * 64;
+        float sn, cs;
+        rope_sincos(pos, tid, 64, log2_base, &sn, &cs);
+        const float x1 = bf2f(ks[tid]), x2 = bf2f(ks[tid + 32]);
+        const size_t off = ((size_t)b * S + slot) * rs + (size_t)g * 64;
+        kc[off + tid] = f2bf(x1 * cs - x2 * sn);
+        kc[off + tid + 32] = f2bf(x2 * cs + x1 * sn);
+        vc[off + tid] = vs[tid];
+        vc[off + tid + 32] = vs[tid + 32];
       }
+      __threadfence_block();
+      __syncthreads();
     }
-    // V tile -> LDS transposed: lane = key, 8 chunks of 8 dims.
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, G = lane >> 4;
+    // Q^T fragment (B operand): lane holds head n of the group, dims 8G+e and 32+8G+e.
+    bf16x8_v qf[2];
     {
-      const int key = j0 + lane;
+      const bf16_t* src = q + ((size_t)b * Hq + g * grp + min(n, grp - 1)) * 64;
+      const uint4 r0 = *(const uint4*)(src + 8 * G);
+      const uint4 r1 = *(const uint4*)(src + 32 + 8 * G);
+      const bf16_t* p0 = (const bf16_t*)&r0;
+      const bf16_t* p1 = (const bf16_t*)&r1;
+      const float qs = n < grp ? qscale : 0.f;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        uint4 val = {0u, 0u, 0u, 0u};
-        if (key < L) val = *(const uint4*)(vbase + (size_t)key * rs + 8 * r);
-        const bf16_t* pv = (const bf16_t*)&val;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sVt[wave][(8 * r + e) * kVRow + lane] = pv[e];
+      for (int e = 0; e < 8; ++e) {
+        float sn, cs;
+        rope_sincos(pos, 8 * G + e, 64, log2_base, &sn, &cs);
+        const float x1 = bf2f(p0[e]), x2 = bf2f(p1[e]);
+        qf[0][e] = (__bf16)((x1 * cs - x2 * sn) * qs);
+        qf[1][e] = (__bf16)((x2 * cs + x1 * sn) * qs);
       }
     }
-    f32x4_v sc[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[kb][i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[s], sc[kb], 0, 0, 0);
-    }
-    const float NEG_INF = -__builtin_huge_valf();
-    float mx = NEG_INF;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = j0 + 32 * (kb >> 1) + 8 * G + 4 * (kb & 1) + i;
-        if (key >= L) sc[kb][i] = NEG_INF;
-        mx = fmaxf(mx, sc[kb][i]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    m_run = mx;
-    bf16x8_v pf[2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = fast_exp2(sc[kb][i] - mx);
-        l_run += p;
-        pf[kb >> 1][4 * (kb & 1) + i] = (__bf16)p;
-      }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int j0 = (split * 4 + wave) * 64;
+    float m_run = -1e30f, l_run = 0.f;
+    f32x4_v acc[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8_v a = *(const bf16x8_v*)(&sVt[wave][(16 * db + n) * kVRow + 32 * s + 8 * G]);
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[s], acc[db], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) acc[db][i] = 0.f;
+    if (j0 < L) {
+      const bf16_t* kbase = kc + ((size_t)b * S) * rs + (size_t)g * 64;
+      const bf16_t* vbase = vc + ((size_t)b * S) * rs + (size_t)g * 64;
+      // All 16 loads of the tile are unconditional (rows past L are clamped and
+      // masked afterwards), so they are all in flight together.
+      bf16x8_v kf[4][2];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int key = min(j0 + 32 * (kb >> 1) + 8 * (n >> 2) + 4 * (kb & 1) + (n & 3), L - 1);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          kf[kb][s] = *(const bf16x8_v*)(kbase + (size_t)key * rs + 32 * s + 8 * G);
       }
-  }
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (G == 0) {
-    sm[wave][n] = m_run;
-    sl[wave][n] = l_run;
-  }
+      uint4 vr[8];
+      {
+        const int key = min(j0 + lane, L - 1);
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+        for (int r = 0; r < 8; ++r) vr[r] = *(const uint4*)(vbase + (size_t)key * rs + 8 * r);
+      }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sO[wave][n][16 * db + 4 * G + i] = acc[db][i];
-  __syncthreads();
-  float* dst = part + ((size_t)pair * n_split + split) * grp * 66;
-  for (int idx = threadIdx.x; idx < grp * 64; idx += 256) {
-    const int hh = idx >> 6, d = idx & 63;
-    float M = sm[0][hh];
+      for (int r = 0; r < 8; ++r) {
+        const bf16_t* pv = (const bf16_t*)&vr[r];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm[w][hh]);
-    float Ls = 0.f, O = 0.f;
+        for (int e = 0; e < 8; ++e) sVt[wave][(8 * r + e) * kVRow + lane] = pv[e];
+      }
+      f32x4_v sc[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = fast_exp2(sm[w][hh] - M);
-      Ls += sl[w][hh] * f;
-      O += sO[w][hh][d] * f;
+      for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[kb][i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[s], sc[kb], 0, 0, 0);
+      }
+      const float NEG_INF = -__builtin_huge_valf();
+      float mx = NEG_INF;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = j0 + 32 * (kb >> 1) + 8 * G + 4 * (kb & 1) + i;
+          if (key >= L) sc[kb][i] = NEG_INF;
+          mx = fmaxf(mx, sc[kb][i]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      m_run = mx;
+      bf16x8_v pf[2];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = fast_exp2(sc[kb][i] - mx);
+          l_run += p;
+          pf[kb >> 1][4 * (kb & 1) + i] = (__bf16)p;
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8_v a = *(const bf16x8_v*)(&sVt[wave][(16 * db + n) * kVRow + 32 * s + 8 * G]);
+          acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[s], acc[db], 0, 0, 0);
+        }
     }
-    float* ph = dst + hh * 66;
-    if (d == 0) {
-      ph[0] = M;
-      ph[1] = Ls;
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (G == 0) {
+      sm[wave][n] = m_run;
+      sl[wave][n] = l_run;
     }
-    ph[2 + d] = O;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sO[wave][n][16 * db + 4 * G + i] = acc[db][i];
+    __syncthreads();
+    float* dst = part + (size_t)b * part_b_stride + ((size_t)g * n_split + split) * grp * 66;
+    for (int idx = tid; idx < grp * 64; idx += 256) {
+      const int hh = idx >> 6, d = idx & 63;
+      float M = sm[0][hh];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) M = fmaxf(M, sm[w][hh]);
+      float Ls = 0.f, O = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = fast_exp2(sm[w][hh] - M);
+        Ls += sl[w][hh] * f;
+        O += sO[w][hh][d] * f;
+      }
+      float* ph = dst + hh * 66;
+      if (d == 0) {
+        ph[0] = M;
+        ph[1] = Ls;
+      }
+      ph[2 + d] = O;
+    }
+  } else {
+    const int sb = blockIdx.x - n_attn;
+    const int b = sb / ssm_per_b;
+    const int c = (sb % ssm_per_b) * 256 + tid;
+    if (c < Di)
+      ys_ws[(size_t)b * ys_stride + c] =
+          ssm_step_one<bf16_t>(b, c, Di, x, dl, Bm, Cm, z, A, D, cw, cb, conv_state, ssm_state);
   }
 }
 
@@ -268,7 +353,8 @@ template <int DH>
 __global__ __launch_bounds__(64) void step_attn_f32(const float* __restrict__ q,
                                                     const float* __restrict__ kc,
                                                     const float* __restrict__ vc,
-                                                    float* __restrict__ part, int B, int Hq,
+                                                    float* __restrict__ part,
+                                                    size_t part_b_stride, int B, int Hq,
                                                     int Hkv, int S, int L, long long pos,
                                                     float qscale, double log2_base) {
   const int idx = blockIdx.x * 64 + threadIdx.x;
@@ -302,70 +388,52 @@ __global__ __launch_bounds__(64) void step_attn_f32(const float* __restrict__ q,
     for (int d = 0; d < DH; ++d) acc[d] = acc[d] * alpha + p * vr[d];
     m = mn;
   }
-  float* ph = part + ((size_t)(b * Hkv + g) * grp + (h % grp)) * (DH + 2);
+  float* ph = part + (size_t)b * part_b_stride + ((size_t)g * grp + (h % grp)) * (DH + 2);
   ph[0] = m;
   ph[1] = l;
 #pragma unroll
   for (int d = 0; d < DH; ++d) ph[2 + d] = acc[d];
 }
 
-// ---------------------------------------------------------------- combine + fusion
+// SSM step + producer KV write (f32 path)
 template <typename Tact>
-__global__ __launch_bounds__(256) void step_combine(
-    const float* __restrict__ part, const float* __restrict__ ys_ws,
-    const float* __restrict__ ba, const float* __restrict__ bs, float eps, Tact* __restrict__ out,
-    float* __restrict__ ya_out, float* __restrict__ ys_out, int Hq, int Hkv, int Dh,
-    int n_split, int Di) {
-  __shared__ float sya[4096];
-  __shared__ float red[2][4];
-  const int b = blockIdx.x;
-  const int grp = Hq / Hkv;
-  const int stride = Dh + 2;
-  float sa = 0.f, ss = 0.f;
-  for (int idx = threadIdx.x; idx < Di; idx += 256) {
-    const int h = idx / Dh, d = idx % Dh;
-    const int g = h / grp, hh = h % grp;
-    const float* base = part + ((size_t)(b * Hkv + g) * n_split) * grp * stride + hh * stride;
-    float M = base[0];
-    for (int s = 1; s < n_split; ++s) M = fmaxf(M, base[(size_t)s * grp * stride]);
-    float Ls = 0.f, O = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float* ps = base + (size_t)s * grp * stride;
-      const float f = fast_exp2(ps[0] - M);
-      Ls += ps[1] * f;
-      O += ps[2 + d] * f;
-    }
-    const float ya = O / Ls;
-    sya[idx] = ya;
-    sa += ya * ya;
-    const float yv = ys_ws[(size_t)b * Di + idx];
-    ss += yv * yv;
+__global__ __launch_bounds__(256) void step_ssm_kv(
+    const Tact* __restrict__ x, const Tact* __restrict__ dl, const Tact* __restrict__ Bm,
+    const Tact* __restrict__ Cm, const Tact* __restrict__ z, const float* __restrict__ A,
+    const float* __restrict__ D, const float* __restrict__ cw, const float* __restrict__ cb,
+    float* __restrict__ conv_state, float* __restrict__ ssm_state, float* __restrict__ ys_ws,
+    size_t ys_stride, int B, int Di, int n_ssm_blocks, const Tact* __restrict__ k_new,
+    const Tact* __restrict__ v_new, Tact* __restrict__ k_cache, Tact* __restrict__ v_cache,
+    int Hkv, int Dh, int S, int slot, long long pos, double log2_base) {
+  if ((int)blockIdx.x < n_ssm_blocks) {
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)B * Di) return;
+    const int c = idx % Di, b = idx / Di;
+    ys_ws[(size_t)b * ys_stride + c] =
+        ssm_step_one<Tact>(b, c, Di, x, dl, Bm, Cm, z, A, D, cw, cb, conv_state, ssm_state);
+    return;
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    sa += __shfl_xor(sa, off);
-    ss += __shfl_xor(ss, off);
-  }
-  if ((threadIdx.x & 63) == 0) {
-    red[0][threadIdx.x >> 6] = sa;
-    red[1][threadIdx.x >> 6] = ss;
-  }
-  __syncthreads();
-  sa = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-  ss = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-  const float ra = 0.5f / sqrtf(sa / (float)Di + eps);
-  const float rs = 0.5f / sqrtf(ss / (float)Di + eps);
-  for (int idx = threadIdx.x; idx < Di; idx += 256) {
-    const float ya = sya[idx];
-    const float yv = ys_ws[(size_t)b * Di + idx];
-    ActIO<Tact>::st(out + (size_t)b * Di + idx, ba[idx] * ya * ra + bs[idx] * yv * rs);
-    if (ya_out) ya_out[(size_t)b * Di + idx] = ya;
-    if (ys_out) ys_out[(size_t)b * Di + idx] = yv;
-  }
+  const long long idx = (long long)(blockIdx.x - n_ssm_blocks) * 256 + threadIdx.x;
+  const int half = Dh / 2;
+  if (idx >= (long long)B * Hkv * half) return;
+  const int d = idx % half;
+  const int g = (idx / half) % Hkv;
+  const int b = idx / ((long long)half * Hkv);
+  const Tact* ks = k_new + ((size_t)b * Hkv + g) * Dh;
+  const Tact* vs = v_new + ((size_t)b * Hkv + g) * Dh;
+  float sn, cs;
+  rope_sincos(pos, d, Dh, log2_base, &sn, &cs);
+  const float x1 = ldx(ks + d), x2 = ldx(ks + d + half);
+  const size_t off = (((size_t)b * S + slot) * Hkv + g) * Dh;
+  ActIO<Tact>::st(k_cache + off + d, x1 * cs - x2 * sn);
+  ActIO<Tact>::st(k_cache + off + d + half, x2 * cs + x1 * sn);
+  v_cache[off + d] = vs[d];
+  v_cache[off + d + half] = vs[d + half];
 }
 
 struct StepGeom {
   int L, n_split, grp;
+  size_t ys_stride, part_b_stride;            // floats per sequence
   size_t ys_bytes, part_bytes;
 };
 
@@ -376,8 +444,10 @@ StepGeom step_geom(const hm_step_args* a) {
   s.L = (int)(a->n_meta + nv);
   s.grp = a->Hkv > 0 ? a->Hq / a->Hkv : 0;
   s.n_split = a->dtype == HM_BF16 ? (s.L + kKeysPerWG - 1) / kKeysPerWG : 1;
-  s.ys_bytes = hm::align_up((size_t)a->B * a->Di * sizeof(float), 256);
-  s.part_bytes = (size_t)a->B * a->Hkv * s.n_split * s.grp * (a->Dh + 2) * sizeof(float);
+  s.ys_stride = hm::align_up((size_t)a->Di, 64);
+  s.part_b_stride = hm::align_up((size_t)a->Hkv * s.n_split * s.grp * (a->Dh + 2), 64);
+  s.ys_bytes = (size_t)a->B * s.ys_stride * sizeof(float);
+  s.part_bytes = (size_t)a->B * s.part_b_stride * sizeof(float);
   return s;
 }
 
@@ -446,10 +516,13 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
     HM_PTR(a->k_new);
     HM_PTR(a->v_new);
   }
-  HM_REQUIRE((double)a->B * (a->n_meta + a->cache_slots) * a->Hkv * a->Dh < 4.0e9,
+  HM_REQUIRE((double)a->B * (a->n_meta + a->cache_slots) * a->Hkv * a->Dh < 4.0e9 &&
+                 (double)a->B * a->Hkv * (a->n_meta + a->cache_slots) / kKeysPerWG < 1.0e9,
              HM_ERR_UNSUPPORTED, "cache too large");
   const StepGeom g = step_geom(a);
   const size_t need = g.ys_bytes + g.part_bytes;
+  HM_REQUIRE((size_t)a->Hq * g.n_split <= (size_t)kCombMaxW, HM_ERR_UNSUPPORTED,
+             "too many query heads x key splits for the combine");
   HM_REQUIRE(a->workspace != nullptr && a->workspace_bytes >= need && hm::aligned16(a->workspace),
              HM_ERR_WORKSPACE, "workspace smaller than hm_mixer_step_workspace()");
 
@@ -461,34 +534,32 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
   const int slot = (int)hm_debug_cache_slot(a->n_prev, a->n_meta, a->window);
   const double l2b = log2((double)a->rope_base);
   const float sc = (a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)a->Dh)) * kLog2e;
+
+  if (a->dtype == HM_BF16) {
+    const int n_attn = a->B * a->Hkv * g.n_split;
+    const int ssm_per_b = (a->Di + 255) / 256;
+    hipLaunchKernelGGL(step_fused_bf16, dim3(n_attn + a->B * ssm_per_b), dim3(256), 0, st,
+                       (const bf16_t*)a->q, (const bf16_t*)a->k_new, (const bf16_t*)a->v_new,
+                       (bf16_t*)a->k_cache, (bf16_t*)a->v_cache, (const bf16_t*)a->x,
+                       (const bf16_t*)a->delta, (const bf16_t*)a->Bm, (const bf16_t*)a->Cm,
+                       (const bf16_t*)a->z, a->A, a->D, a->conv_w, a->conv_b, a->conv_state,
+                       a->ssm_state, ys_ws, g.ys_stride, part, g.part_b_stride, a->Hq, a->Hkv,
+                       a->Di, S, g.L, slot, pos, sc, l2b, g.n_split, n_attn, ssm_per_b);
+    hm_status s = hm::check_launch("step_fused_bf16");
+    if (s != HM_OK) return s;
+    hipLaunchKernelGGL(step_combine<bf16_t>, dim3(a->B), dim3(kCombThreads), 0, st,
+                       (const float*)part, g.part_b_stride, (const float*)ys_ws, g.ys_stride,
+                       a->beta_a, a->beta_s, a->eps, (bf16_t*)a->out, a->ya_out, a->ys_out, a->Hq,
+                       a->Hkv, a->Dh, g.n_split, a->Di);
+    return hm::check_launch("step_combine");
+  }
   const int n_ssm_blocks = (int)(((long long)a->B * a->Di + 255) / 256);
   const int n_kv_blocks =
       producer ? (int)(((long long)a->B * a->Hkv * (a->Dh / 2) + 255) / 256) : 0;
-
-  if (a->dtype == HM_BF16) {
-    hipLaunchKernelGGL(step_ssm_kv<bf16_t>, dim3(n_ssm_blocks + n_kv_blocks), dim3(256), 0, st,
-                       (const bf16_t*)a->x, (const bf16_t*)a->delta, (const bf16_t*)a->Bm,
-                       (const bf16_t*)a->Cm, (const bf16_t*)a->z, a->A, a->D, a->conv_w,
-                       a->conv_b, a->conv_state, a->ssm_state, ys_ws, a->B, a->Di, n_ssm_blocks,
-                       (const bf16_t*)a->k_new, (const bf16_t*)a->v_new, (bf16_t*)a->k_cache,
-                       (bf16_t*)a->v_cache, a->Hkv, a->Dh, S, slot, pos, l2b);
-    hm_status s = hm::check_launch("step_ssm_kv");
-    if (s != HM_OK) return s;
-    hipLaunchKernelGGL(step_attn_bf16, dim3(g.n_split, a->B * a->Hkv), dim3(256), 0, st,
-                       (const bf16_t*)a->q, (const bf16_t*)a->k_cache,
-                       (const bf16_t*)a->v_cache, part, a->Hq, a->Hkv, S, g.L, pos, sc, l2b,
-                       g.n_split);
-    s = hm::check_launch("step_attn_bf16");
-    if (s != HM_OK) return s;
-    hipLaunchKernelGGL(step_combine<bf16_t>, dim3(a->B), dim3(256), 0, st, (const float*)part,
-                       (const float*)ys_ws, a->beta_a, a->beta_s, a->eps, (bf16_t*)a->out,
-                       a->ya_out, a->ys_out, a->Hq, a->Hkv, a->Dh, g.n_split, a->Di);
-    return hm::check_launch("step_combine");
-  }
   hipLaunchKernelGGL(step_ssm_kv<float>, dim3(n_ssm_blocks + n_kv_blocks), dim3(256), 0, st,
                      (const float*)a->x, (const float*)a->delta, (const float*)a->Bm,
                      (const float*)a->Cm, (const float*)a->z, a->A, a->D, a->conv_w, a->conv_b,
-                     a->conv_state, a->ssm_state, ys_ws, a->B, a->Di, n_ssm_blocks,
+                     a->conv_state, a->ssm_state, ys_ws, g.ys_stride, a->B, a->Di, n_ssm_blocks,
                      (const float*)a->k_new, (const float*)a->v_new, (float*)a->k_cache,
                      (float*)a->v_cache, a->Hkv, a->Dh, S, slot, pos, l2b);
   hm_status s = hm::check_launch("step_ssm_kv");
@@ -497,8 +568,8 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
 #define HM_STEP_F32(DHV)                                                                      \
   case DHV:                                                                                   \
     hipLaunchKernelGGL(step_attn_f32<DHV>, dim3(nbh), dim3(64), 0, st, (const float*)a->q,   \
-                       (const float*)a->k_cache, (const float*)a->v_cache, part, a->B, a->Hq,  \
-                       a->Hkv, S, g.L, pos, sc, l2b);                                          \
+                       (const float*)a->k_cache, (const float*)a->v_cache, part,               \
+                       g.part_b_stride, a->B, a->Hq, a->Hkv, S, g.L, pos, sc, l2b);            \
     break;
   switch (a->Dh) {
     HM_STEP_F32(16)
@@ -508,9 +579,9 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
 #undef HM_STEP_F32
   s = hm::check_launch("step_attn_f32");
   if (s != HM_OK) return s;
-  hipLaunchKernelGGL(step_combine<float>, dim3(a->B), dim3(256), 0, st, (const float*)part,
-                     (const float*)ys_ws, a->beta_a, a->beta_s, a->eps, (float*)a->out, a->ya_out,
-                     a->ys_out, a->Hq, a->Hkv, a->Dh, 1, a->Di);
+  hipLaunchKernelGGL(step_combine<float>, dim3(a->B), dim3(kCombThreads), 0, st, (const float*)part,
+                     g.part_b_stride, (const float*)ys_ws, g.ys_stride, a->beta_a, a->beta_s,
+                     a->eps, (float*)a->out, a->ya_out, a->ys_out, a->Hq, a->Hkv, a->Dh, 1, a->Di);
   return hm::check_launch("step_combine");
 }
 

@@ -82,6 +82,24 @@ hm_status hm_swa_meta_attn(const void* q, const void* k, const void* v, void* o,
                            void* stream);
 size_t hm_swa_meta_attn_workspace(int B, int T, int Hkv, int Dh, hm_dtype dtype);
 
+/* The two halves of hm_swa_meta_attn, so that the prepared K/V of one layer
+ * can serve the next layer (adjacent layers share their KV: Hymba blog,
+ * Hymba 的整体架构) and so that the attention kernel can run on its own.
+ *   hm_attn_kv_prepare: rotate k (RoPE at positions pos0 + i) and lay out k and
+ *     v for the attention kernel in `kv` (hm_attn_kv_bytes() bytes, caller-owned).
+ *   hm_attn_with_kv: attention of q over a prepared `kv`.  rope_base and pos0
+ *     must be the values the buffer was prepared with; k and v are not needed.
+ * The layout of `kv` is private to the library (bf16: rotated K as
+ * [B, Hkv, ceil(T/64)*64, 64] followed by V as 64x64 tiles transposed per
+ * head; f32: rotated K [B, Hkv, T, Dh] followed by a copy of V). */
+size_t hm_attn_kv_bytes(int B, int T, int Hkv, int Dh, hm_dtype dtype);
+hm_status hm_attn_kv_prepare(const void* k, const void* v, void* kv, size_t kv_bytes, int B,
+                             int T, int Hkv, int Dh, float rope_base, long long pos0,
+                             hm_dtype dtype, void* stream);
+hm_status hm_attn_with_kv(const void* q, const void* kv, size_t kv_bytes, void* o, int B, int T,
+                          int Hq, int Hkv, int Dh, int n_meta, int window, float rope_base,
+                          long long pos0, float scale, hm_dtype dtype, void* stream);
+
 /* ------------------------------------------------------------------------
  * Causal depthwise conv1d in front of the scan (the short convolution of a
  * Mamba head; not printed on the pages):
@@ -139,12 +157,20 @@ hm_status hm_branch_norm_mean(const void* ya, const void* ys, const float* beta_
                               long long rows, int width, hm_dtype dtype, void* stream);
 
 /* ------------------------------------------------------------------------
- * One whole mixer layer in prefill: attention (hm_swa_meta_attn) and the SSM
- * branch (hm_conv_selective_scan from zero states) on the same X~, then
+ * One whole mixer layer in prefill: attention and the SSM branch
+ * (hm_conv_selective_scan from zero states) on the same X~, then
  * hm_branch_norm_mean.  Width Di must equal Hq * Dh.
  * ya, ys: [B, T, Di] branch outputs (written; caller-owned, act dtype);
  * out: [B, T, Di].  conv_state_out [B, Di, K-1] and h_out [B, Di, N] (f32,
  * may be NULL) receive the final SSM-branch states for a following decode.
+ * Prepared K/V: `kv` (hm_attn_kv_bytes() bytes, optional).  kv_reuse == 0:
+ * k and v are prepared into kv (or into the workspace when kv is NULL);
+ * kv_reuse != 0: kv already holds the K/V prepared by an earlier layer with
+ * the same B, T, Hkv, Dh, rope_base and pos0 (the adjacent-layer KV sharing)
+ * and k, v are not read.
+ * stream2 (optional, a hipStream_t as void*): when set, the SSM branch runs on
+ * it, concurrently with attention on `stream` (the two head types are
+ * independent until the fusion); `stream` waits for it before the fusion.
  * Workspace: hm_mixer_prefill_workspace() bytes.
  * ---------------------------------------------------------------------- */
 typedef struct {
@@ -158,6 +184,10 @@ typedef struct {
   const float *beta_a, *beta_s;               /* [Di] */
   void *ya, *ys, *out;                        /* [B,T,Di] each */
   float *conv_state_out, *h_out;              /* optional */
+  void* kv;                                   /* optional prepared K/V */
+  size_t kv_bytes;
+  int kv_reuse;
+  void* stream2;                              /* optional second stream */
   void* workspace;
   size_t workspace_bytes;
 } hm_prefill_args;
@@ -182,7 +212,9 @@ size_t hm_mixer_prefill_workspace(const hm_prefill_args* a);
  * one token in place; out = branch norm-and-average of the two branches.
  * Optional ya_out / ys_out ([B, Di] f32) receive the branch outputs.
  * Supported: bf16 with Dh = 64 (MFMA), f32 with Dh in {16, 32, 64}; N = 16; K = 4.
- * Workspace: hm_mixer_step_workspace() bytes.
+ * Workspace: hm_mixer_step_workspace() bytes (per-split partials and the SSM
+ * branch output).  Calls that share a workspace must not overlap (stream-
+ * ordered calls are fine).
  * ---------------------------------------------------------------------- */
 typedef struct {
   int B, Hq, Hkv, Dh, Di, N, K, n_meta, window, cache_slots;

@@ -47,7 +47,8 @@ def test_cache_slot_matches_oracle():
 def test_workspace_queries():
     L = hm.lib
     assert L.hm_swa_meta_attn_workspace(1, 2176, 5, 64, hm.HM_BF16) == 2 * 5 * 2176 * 64 * 2
-    assert L.hm_swa_meta_attn_workspace(1, 64, 1, 16, hm.HM_F32) == 64 * 16 * 4
+    assert L.hm_swa_meta_attn_workspace(1, 64, 1, 16, hm.HM_F32) == 2 * 64 * 16 * 4
+    assert L.hm_attn_kv_bytes(1, 2176, 5, 64, hm.HM_BF16) == 2 * 5 * 2176 * 64 * 2
     assert L.hm_swa_meta_attn_workspace(0, 64, 1, 16, hm.HM_F32) == 0
     assert L.hm_selective_scan_workspace(1, 2176, 1600, 16) > 0
     assert L.hm_selective_scan_workspace(1, 2176, 1600, 8) == 0
@@ -66,8 +67,8 @@ def _err():
 
 def test_attention_rejects_bad_arguments():
     L = hm.lib
-    args = [FAKE, FAKE, FAKE, ctypes.c_void_p(2 << 20), 1, 64, 2, 1, 16, 4, 16, 1e4, 0, 0.0,
-            hm.HM_F32, FAKE, 1 << 30, None]
+    q, k, v, o, ws = (ctypes.c_void_p(i << 20) for i in range(1, 6))
+    args = [q, k, v, o, 1, 64, 2, 1, 16, 4, 16, 1e4, 0, 0.0, hm.HM_F32, ws, 1 << 30, None]
     bad = list(args); bad[0] = None
     assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_INVALID and "q" in _err()
     bad = list(args); bad[7] = 3                      # Hq % Hkv != 0 (Hq=2, Hkv=3)
@@ -80,7 +81,7 @@ def test_attention_rejects_bad_arguments():
     assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_UNSUPPORTED
     bad = list(args); bad[16] = 16                    # short workspace
     assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_WORKSPACE
-    bad = list(args); bad[3] = FAKE                   # o aliases q
+    bad = list(args); bad[3] = q                      # o aliases q
     assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_INVALID
     bad = list(args); bad[1] = ctypes.c_void_p((1 << 20) + 4)   # misaligned k
     assert L.hm_swa_meta_attn(*bad) == hm.HM_ERR_INVALID
@@ -123,3 +124,29 @@ def test_step_and_prefill_reject_bad_arguments():
                        rope_base=1e4, eps=1e-6, dtype=hm.HM_F32)
     assert L.hm_mixer_prefill(ctypes.byref(p), None) == hm.HM_ERR_INVALID   # NULL outputs
     assert L.hm_mixer_prefill(None, None) == hm.HM_ERR_INVALID
+
+
+def test_ctypes_structs_match_the_header(tmp_path):
+    """The binding's hm_prefill_args / hm_step_args layouts equal the C ones."""
+    import shutil
+    import subprocess
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    src = tmp_path / "sz.cpp"
+    fields_p = [f for f, _ in hm.PrefillArgs._fields_]
+    fields_s = [f for f, _ in hm.StepArgs._fields_]
+    lines = ['#include "hm.h"', "#include <cstdio>", "#include <cstddef>", "int main() {",
+             'printf("%zu %zu\\n", sizeof(hm_prefill_args), sizeof(hm_step_args));']
+    lines += [f'printf("%zu\\n", offsetof(hm_prefill_args, {f}));' for f in fields_p]
+    lines += [f'printf("%zu\\n", offsetof(hm_step_args, {f}));' for f in fields_s]
+    lines += ["return 0; }"]
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "sz"
+    subprocess.run([cxx, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    vals = [int(v) for v in out]
+    assert vals[0] == ctypes.sizeof(hm.PrefillArgs) and vals[1] == ctypes.sizeof(hm.StepArgs)
+    offs = vals[2:]
+    assert offs[:len(fields_p)] == [getattr(hm.PrefillArgs, f).offset for f in fields_p]
+    assert offs[len(fields_p):] == [getattr(hm.StepArgs, f).offset for f in fields_s]

@@ -176,7 +176,8 @@ def test_conv_selective_scan(shape, use_state):
 
 @pytest.mark.parametrize("dtype,width,rows", [("f32", 32, 64), ("bf16", 1600, 2176),
                                               ("bf16", 1600, 3), ("f32", 37, 5),
-                                              ("bf16", 200, 9)])
+                                              ("bf16", 200, 9), ("bf16", 2400, 7),
+                                              ("f32", 2048, 6)])
 def test_branch_norm_mean(dtype, width, rows):
     rng = np.random.default_rng(width)
     from workloads import bf16_round
@@ -202,3 +203,37 @@ def test_mixer_prefill(shape):
     for k in ("ya", "ys", "out", "ssm_state"):
         assert_close(down(r[k]), ref[k], shape.dtype, f"mixer {k}")
     assert np.array_equal(down(r["conv_state"]), ref["conv_state"])
+
+
+# ------------------------------------------------------------------ prepared K/V, two streams
+def test_prepared_kv_shared_between_layers():
+    shape = with_(SWA_PREFILL, N=500, M=16, W=128)
+    prod, cons = prefill_inputs(shape, 10), prefill_inputs(shape, 11)
+    tp, tc = up_inputs(prod, "bf16"), up_inputs(cons, "bf16")
+    kv = hm.attn_kv_prepare(tp["k"], tp["v"])
+    o = hm.attn_with_kv(tc["q"], kv, shape.Hkv, shape.M, shape.W)
+    ref = oracle.attention(cons["q"], prod["k"], prod["v"], shape.M, shape.W)
+    assert_close(down(o), ref, "bf16", "consumer attention over producer K/V")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mixer_prefill_two_streams_and_kv_reuse(dtype):
+    shape = with_(SWA_PREFILL, N=700, M=64, W=256, dtype=dtype) if dtype == "bf16" else \
+        with_(TINY, N=200, Hq=4, Hkv=2, Di=64)
+    prod, cons = prefill_inputs(shape, 12), prefill_inputs(shape, 13)
+    tp, tc = up_inputs(prod, dtype), up_inputs(cons, dtype)
+    del tc["k"], tc["v"]
+    tc["Hkv"] = shape.Hkv
+    s2 = torch.cuda.Stream()
+    p1 = hm.PrefillPlan(tp, shape.M, shape.W, stream2=s2)
+    p2 = hm.PrefillPlan(tc, shape.M, shape.W, kv=p1.kv, kv_reuse=True, stream2=s2)
+    for _ in range(2):       # a second run reuses the same buffers and events
+        p1.run()
+        p2.run()
+    torch.cuda.synchronize()
+    mixed = dict(cons)
+    mixed["k"], mixed["v"] = prod["k"], prod["v"]
+    for plan, src in ((p1, prod), (p2, mixed)):
+        ref = oracle.mixer_prefill(src, shape.M, shape.W)
+        for k, got in (("ya", plan.ya), ("ys", plan.ys), ("out", plan.out), ("ssm_state", plan.h)):
+            assert_close(down(got), ref[k], dtype, f"{k}")

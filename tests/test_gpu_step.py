@@ -81,3 +81,28 @@ def test_decode_pair_bf16_global(n_prev):
 def test_decode_pair_f32(n_prev, Dh):
     shape = with_(TINY, B=2, n_prev=n_prev, cache_slots=16, Dh=Dh, Di=2 * Dh)
     _check(shape, 3)
+
+
+def test_decode_repeated_calls_reuse_workspace():
+    """Three tokens in a row through the same plans (same workspace, states
+    advancing in place) against the oracle stepped three times."""
+    shape = with_(DECODE_PAIR, B=4, n_prev=700)
+    d = decode_inputs(shape, 5)
+    t = up_inputs(d, shape.dtype)
+    pa = hm.StepPlan(t["a"], t["k_cache"], t["v_cache"], shape.n_prev, shape.M, shape.W)
+    pb = hm.StepPlan(t["b"], t["k_cache"], t["v_cache"], shape.n_prev, shape.M, shape.W)
+    la, lb = dict(d["a"]), dict(d["b"])
+    kc, vc = d["k_cache"], d["v_cache"]
+    for it in range(3):
+        pa.run()
+        pb.run()
+        torch.cuda.synchronize()
+        ra = oracle.mixer_step(la, kc, vc, shape.n_prev, shape.M, shape.W, producer=True)
+        rb = oracle.mixer_step(lb, ra["k_cache"], ra["v_cache"], shape.n_prev, shape.M, shape.W,
+                               producer=False)
+        assert_close(down(pa.out), ra["out"], "bf16", f"producer out, call {it}")
+        assert_close(down(pb.out), rb["out"], "bf16", f"consumer out, call {it}")
+        la["conv_state"], la["ssm_state"] = ra["conv_state"], ra["ssm_state"]
+        lb["conv_state"], lb["ssm_state"] = rb["conv_state"], rb["ssm_state"]
+        kc, vc = ra["k_cache"], ra["v_cache"]
+    assert_close(down(t["a"]["ssm_state"]), la["ssm_state"], "bf16", "state after 3 calls")

@@ -2,4 +2,4 @@
 from .configs import (ALL, DECODE_PAIR, GLOBAL_PREFILL, STACK, SWA_PREFILL, TINY,
                       MixerShape, stack_layer_roles, with_)
 from .inputs import (bf16_bits, bf16_round, decode_inputs, prefill_inputs,
-                     prefill_inputs_torch)
+                     prefill_inputs_torch, to_device)

@@ -144,3 +144,22 @@ def prefill_inputs_torch(shape: MixerShape, seed: int, layer: int, device):
     out["beta_a"] = 1.0 + 0.1 * n(Di)
     out["beta_s"] = 1.0 + 0.1 * n(Di)
     return out
+
+
+ACT_KEYS = ("q", "k", "v", "x", "delta", "Bm", "Cm", "z", "k_new", "v_new", "k_cache", "v_cache")
+
+
+def to_device(d: dict, dtype: str, device="cuda") -> dict:
+    """Upload generator output: activations in the workload dtype (exact bf16
+    bit patterns), parameters and states as float32.  Nested dicts recurse."""
+    import torch
+
+    out = {}
+    for k, v in d.items():
+        if isinstance(v, dict):
+            out[k] = to_device(v, dtype, device)
+        elif k in ACT_KEYS and dtype == "bf16":
+            out[k] = torch.from_numpy(bf16_bits(v).view(np.int16)).view(torch.bfloat16).to(device)
+        else:
+            out[k] = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(device)
+    return out
