@@ -3,9 +3,10 @@
 
 A step is one prefill pass of one mixer layer (RoPE, the meta + sliding-window
 GQA attention, the causal conv + selective scan branch, the branch norm and
-average) over the sliding-window workload: batch 1, 128 meta + 2048 tokens,
-25 query heads x 64, 5 KV heads, window 1024, SSM width 1600 x 16 states,
-bf16 inputs with float32 accumulation, synthetic seeded inputs resident in HBM.
+average; all kernels in order on one stream) over the sliding-window
+workload: batch 1, 128 meta + 2048 tokens, 25 query heads x 64, 5 KV heads,
+window 1024, SSM width 1600 x 16 states, bf16 inputs with float32
+accumulation, synthetic seeded inputs resident in HBM.
 `value` is prefill tokens/s per layer (B * (M + N) rows / step time).
 
 Also reported on the same JSON line:
@@ -21,6 +22,7 @@ Also reported on the same JSON line:
   cpu_baseline  the float64 CPU oracle on one whole layer of the step's workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+                       [--no-cpu-baseline] [--counters]
 """
 from __future__ import annotations
 
@@ -36,6 +38,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+COPY_BYTES = 256 << 20      # calibration copy for the HBM byte counters
 
 
 def attn_flops(shape) -> float:
@@ -111,8 +114,9 @@ def timed(fn, steps: int, warmup: int, stream=None):
     return e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline(shape, inp):
-    """The oracle (float64 NumPy) on one whole prefill layer of the workload."""
+def cpu_baseline(shape, inp, min_seconds: float = 10.0):
+    """The oracle (float64 NumPy) on whole prefill layers of the workload,
+    repeated until at least `min_seconds` of CPU work have been timed."""
     import oracle
     threads = None
     try:
@@ -121,13 +125,18 @@ def cpu_baseline(shape, inp):
         threads = max((d.get("num_threads") or 1) for d in info) if info else 1
     except Exception:
         pass
+    n = 0
     t0 = time.perf_counter()
-    oracle.mixer_prefill(inp, shape.M, shape.W, shape.rope_base, shape.eps)
-    dt = time.perf_counter() - t0
-    return {"value": shape.B * shape.T / dt, "unit": "tokens/s", "cores": threads or 1,
+    while True:
+        oracle.mixer_prefill(inp, shape.M, shape.W, shape.rope_base, shape.eps)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": n * shape.B * shape.T / dt, "unit": "tokens/s", "cores": threads or 1,
             "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"one whole prefill layer of {shape.name} (float64 NumPy), "
-                      f"{dt:.2f} s"}
+            "sample": f"{n} whole prefill layers of {shape.name} (float64 NumPy, same "
+                      f"inputs each time), {dt:.1f} s"}
 
 
 def run_prefill(shape, hm, t, steps, warmup, two_streams):
@@ -163,6 +172,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quick", action="store_true", help="skip the global-prefill and stack lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="only a 256 MiB device copy (calibration) and the attention kernel "
+                         "of the step, for rocprofv3 --pmc runs; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the mixer core runs on a single MI355X here "
@@ -180,9 +192,23 @@ def main():
     inp = prefill_inputs(shape, 0)
     t = to_device(inp, shape.dtype)
 
-    # the step: one mixer layer, both head types on two streams
-    plan, ms = run_prefill(shape, hm, t, args.steps, args.warmup, two_streams=True)
-    _, ms_serial = run_prefill(shape, hm, t, args.steps, args.warmup, two_streams=False)
+    if args.counters:
+        plan = hm.PrefillPlan(t, shape.M, shape.W, rope_base=shape.rope_base, eps=shape.eps)
+        plan.run()
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        for _ in range(3):
+            hm.attn_with_kv(t["q"], plan.kv, shape.Hkv, shape.M, shape.W, shape.rope_base,
+                            out=plan.ya)
+        torch.cuda.synchronize()
+        print("counters run done: 3 copies of", COPY_BYTES, "bytes, 3 attention launches")
+        return
+
+    # the step: one mixer layer (both branches on one stream, kernels in order)
+    plan, ms = run_prefill(shape, hm, t, args.steps, args.warmup, two_streams=False)
+    _, ms_two = run_prefill(shape, hm, t, args.steps, args.warmup, two_streams=True)
     tokens = shape.B * shape.T
 
     # dominant kernel on its own: attention over the prepared K/V
@@ -192,7 +218,7 @@ def main():
     fl = attn_flops(shape)
     achieved = fl / (ms_attn * 1e-3) / 1e12
     traffic = traffic_from_profile("hybrid_head_lm_amd/csrc/attn.hip",
-                                   "attn_fwd_bf16.swa-prefill.pmc.txt")
+                                   "attn_fwd_bf16.swa-prefill-b1-t2176.pmc.txt")
 
     # SSM branch and fusion on their own (context for the breakdown)
     ms_ssm = timed(lambda: hm.conv_selective_scan(t["x"], t["conv_w"], t["conv_b"], t["delta"],
@@ -232,12 +258,12 @@ def main():
                    "tokens": shape.N, "rows": shape.T, "q_heads": shape.Hq,
                    "kv_heads": shape.Hkv, "head_dim": shape.Dh, "window": shape.W,
                    "ssm_width": shape.Di, "ssm_states": shape.Ns, "conv": shape.K,
-                   "branches": "attention and SSM on two streams"},
+                   "branches": "attention then SSM on one stream"},
         "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "algorithmic_flop_per_launch": fl, "ms_per_launch": ms_attn},
-        "breakdown_ms": {"layer_two_streams": ms, "layer_one_stream": ms_serial,
+        "breakdown_ms": {"layer_one_stream": ms, "layer_two_streams": ms_two,
                          "attention_kernel": ms_attn, "ssm_branch": ms_ssm,
                          "norm_mean": ms_norm},
         "ssm_branch": {"bound": "hbm", "achieved": scan_bytes(shape) / (ms_ssm * 1e-3) / 1e9,
@@ -256,7 +282,7 @@ def main():
         gshape = GLOBAL_PREFILL
         gt = to_device(prefill_inputs(gshape, 0), gshape.dtype)
         gsteps = max(3, args.steps // 5)
-        gplan, gms = run_prefill(gshape, hm, gt, gsteps, 2, two_streams=True)
+        gplan, gms = run_prefill(gshape, hm, gt, gsteps, 2, two_streams=False)
         gms_attn = timed(lambda: hm.attn_with_kv(gt["q"], gplan.kv, gshape.Hkv, gshape.M,
                                                  gshape.W, gshape.rope_base, out=gplan.ya),
                          gsteps, 2)
