@@ -75,13 +75,20 @@ __global__ __launch_bounds__(256) void norm_mean_vec(const Tact* __restrict__ ya
   const int n8 = width >> 3;
   float sa = 0.f, ss = 0.f;
   if (n8 <= 64 * kMaxC) {
+    // one round trip to memory: the row of both branches and the beta slices
+    // are all requested before the reduction
     float a[kMaxC][8], s[kMaxC][8];
+    float4 wa[kMaxC][2], wsv[kMaxC][2];
 #pragma unroll
     for (int k = 0; k < kMaxC; ++k) {
       const int c = lane + 64 * k;
       if (c < n8) {
         Vec8<Tact>::ld(pa + 8 * c, a[k]);
         Vec8<Tact>::ld(ps + 8 * c, s[k]);
+        wa[k][0] = *(const float4*)(ba + 8 * c);
+        wa[k][1] = *(const float4*)(ba + 8 * c + 4);
+        wsv[k][0] = *(const float4*)(bs + 8 * c);
+        wsv[k][1] = *(const float4*)(bs + 8 * c + 4);
       }
     }
 #pragma unroll
@@ -100,13 +107,13 @@ __global__ __launch_bounds__(256) void norm_mean_vec(const Tact* __restrict__ ya
     for (int k = 0; k < kMaxC; ++k) {
       const int c = lane + 64 * k;
       if (c < n8) {
-        const float4 ba0 = *(const float4*)(ba + 8 * c), ba1 = *(const float4*)(ba + 8 * c + 4);
-        const float4 bs0 = *(const float4*)(bs + 8 * c), bs1 = *(const float4*)(bs + 8 * c + 4);
-        const float wa[8] = {ba0.x, ba0.y, ba0.z, ba0.w, ba1.x, ba1.y, ba1.z, ba1.w};
-        const float wsv[8] = {bs0.x, bs0.y, bs0.z, bs0.w, bs1.x, bs1.y, bs1.z, bs1.w};
+        const float w1[8] = {wa[k][0].x, wa[k][0].y, wa[k][0].z, wa[k][0].w,
+                             wa[k][1].x, wa[k][1].y, wa[k][1].z, wa[k][1].w};
+        const float w2[8] = {wsv[k][0].x, wsv[k][0].y, wsv[k][0].z, wsv[k][0].w,
+                             wsv[k][1].x, wsv[k][1].y, wsv[k][1].z, wsv[k][1].w};
         float r[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) r[i] = wa[i] * a[k][i] * ra + wsv[i] * s[k][i] * rs;
+        for (int i = 0; i < 8; ++i) r[i] = w1[i] * a[k][i] * ra + w2[i] * s[k][i] * rs;
         Vec8<Tact>::st(po + 8 * c, r);
       }
     }

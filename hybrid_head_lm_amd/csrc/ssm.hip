@@ -27,7 +27,8 @@ namespace {
 
 constexpr int kNS = 16;
 constexpr int kConvK = 4;
-constexpr int kMinChunk = 16;
+constexpr int kSubRows = 16;     // chunk lengths are whole numbers of 16-step sub-blocks
+constexpr int kMinChunk = 32;    // shorter chunks cost more carry traffic than they save
 constexpr int kTargetWaves = 4096;
 
 HM_HD int scan_chunk_len(int B, int T, int Di) {
@@ -37,7 +38,7 @@ HM_HD int scan_chunk_len(int B, int T, int Di) {
   if (nc > maxc) nc = maxc;
   if (nc < 1) nc = 1;
   int L = (T + nc - 1) / nc;
-  L = (L + kMinChunk / 2) / kMinChunk * kMinChunk;   // nearest whole number of sub-blocks
+  L = (L + kSubRows / 2) / kSubRows * kSubRows;   // nearest whole number of sub-blocks
   return L < kMinChunk ? kMinChunk : L;
 }
 
