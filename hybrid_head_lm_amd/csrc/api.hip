@@ -95,10 +95,12 @@ hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream) {
   hipStream_t st2 = a->stream2 ? (hipStream_t)a->stream2 : st;
   HM_REQUIRE(st2 != st || a->stream2 == nullptr, HM_ERR_INVALID, "stream2 must differ from stream");
   // Validate all parts before the first launch, so that a failure leaves
-  // every output untouched.
+  // every output untouched.  bf16 layers on one stream then run the fused
+  // launch sequence; the others run the parts one by one.
   for (int pass = 0; pass < 2; ++pass) {
     const bool dry = pass == 0;
     hm_status s;
+    if (!dry && hm::prefill_fusable(a)) return hm::prefill_fused_bf16(a, kv, ws, st);
     if (!dry && st2 != st) {
       s = hm::fork_join(st, st2, /*fork=*/true);
       if (s != HM_OK) return s;

@@ -148,6 +148,10 @@ hm_status conv_scan_impl(const void* x, const float* conv_w, const float* conv_b
                          float* h_out, int B, int T, int Di, int K, int N, hm_dtype dtype,
                          void* workspace, size_t workspace_bytes, hipStream_t st,
                          bool fuse_conv, bool dry);
+// Fused launch sequence of a bf16 prefill layer (fused.hip); the caller has
+// validated every argument.
+bool prefill_fusable(const hm_prefill_args* a);
+hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, hipStream_t st);
 hm_status norm_mean_impl(const void* ya, const void* ys, const float* beta_a,
                          const float* beta_s, float eps, void* out, long long rows,
                          int width, hm_dtype dtype, hipStream_t st, bool dry);

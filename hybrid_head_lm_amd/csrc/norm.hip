@@ -4,9 +4,8 @@
 // vectors beta_1, beta_2):
 //   out = 0.5 * (beta_a * ya / rms(ya) + beta_s * ys / rms(ys)),
 //   rms(y) = sqrt(mean(y^2) + eps) over the whole branch width of a token.
-// One wave per row: a first pass accumulates both sums of squares in float32
-// (16-byte loads), a wave reduction, then a second pass over the row (served
-// from L1/L2) writes the output.  HBM traffic: read ya and ys once, write out.
+// One wave per row: both sums of squares in float32 (16-byte loads), a wave
+// reduction, then the output row.  HBM traffic: read ya and ys once, write out.
 #include <cmath>
 
 #include "hm_common.h"
@@ -54,10 +53,11 @@ struct Vec8<float> {  // 8 floats = two 16-byte accesses
   }
 };
 
-// width % 8 == 0 (16-byte aligned rows).  Rows of up to 64 * 8 * MAXC
-// elements stay in registers between the two passes (one HBM read per row);
-// wider rows are read twice (the second read is served by L2).
+// Rows of up to 64 * 8 * kMaxC elements are held in registers (norm_mean_rows).
 constexpr int kMaxC = 4;
+
+// width % 8 == 0 (16-byte aligned rows), wider than 64 * 8 * kMaxC: one wave
+// per row; the row is read twice (the second read is served by L2).
 
 template <typename Tact>
 __global__ __launch_bounds__(256) void norm_mean_vec(const Tact* __restrict__ ya,
@@ -74,51 +74,6 @@ __global__ __launch_bounds__(256) void norm_mean_vec(const Tact* __restrict__ ya
   Tact* po = out + row * width;
   const int n8 = width >> 3;
   float sa = 0.f, ss = 0.f;
-  if (n8 <= 64 * kMaxC) {
-    // one round trip to memory: the row of both branches and the beta slices
-    // are all requested before the reduction
-    float a[kMaxC][8], s[kMaxC][8];
-    float4 wa[kMaxC][2], wsv[kMaxC][2];
-#pragma unroll
-    for (int k = 0; k < kMaxC; ++k) {
-      const int c = lane + 64 * k;
-      if (c < n8) {
-        Vec8<Tact>::ld(pa + 8 * c, a[k]);
-        Vec8<Tact>::ld(ps + 8 * c, s[k]);
-        wa[k][0] = *(const float4*)(ba + 8 * c);
-        wa[k][1] = *(const float4*)(ba + 8 * c + 4);
-        wsv[k][0] = *(const float4*)(bs + 8 * c);
-        wsv[k][1] = *(const float4*)(bs + 8 * c + 4);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kMaxC; ++k)
-      if (lane + 64 * k < n8)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          sa += a[k][i] * a[k][i];
-          ss += s[k][i] * s[k][i];
-        }
-    sa = wave_sum(sa);
-    ss = wave_sum(ss);
-    const float ra = 0.5f / sqrtf(sa / (float)width + eps);
-    const float rs = 0.5f / sqrtf(ss / (float)width + eps);
-#pragma unroll
-    for (int k = 0; k < kMaxC; ++k) {
-      const int c = lane + 64 * k;
-      if (c < n8) {
-        const float w1[8] = {wa[k][0].x, wa[k][0].y, wa[k][0].z, wa[k][0].w,
-                             wa[k][1].x, wa[k][1].y, wa[k][1].z, wa[k][1].w};
-        const float w2[8] = {wsv[k][0].x, wsv[k][0].y, wsv[k][0].z, wsv[k][0].w,
-                             wsv[k][1].x, wsv[k][1].y, wsv[k][1].z, wsv[k][1].w};
-        float r[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r[i] = w1[i] * a[k][i] * ra + w2[i] * s[k][i] * rs;
-        Vec8<Tact>::st(po + 8 * c, r);
-      }
-    }
-    return;
-  }
   for (int c = lane; c < n8; c += 64) {
     float a[8], s[8];
     Vec8<Tact>::ld(pa + 8 * c, a);
@@ -144,6 +99,69 @@ __global__ __launch_bounds__(256) void norm_mean_vec(const Tact* __restrict__ ya
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = wa[i] * a[i] * ra + wsv[i] * s[i] * rs;
     Vec8<Tact>::st(po + 8 * c, r);
+  }
+}
+
+// width % 8 == 0 and width <= 64 * 8 * kMaxC: eight rows per workgroup (one per
+// wave), each row held in registers; the two beta vectors are staged in LDS
+// once per workgroup instead of being read by every wave.
+constexpr int kRowsPerBlock = 8;
+
+template <typename Tact>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void norm_mean_rows(
+    const Tact* __restrict__ ya, const Tact* __restrict__ ys, const float* __restrict__ ba,
+    const float* __restrict__ bs, float eps, Tact* __restrict__ out, long long rows, int width) {
+  __shared__ float4 sb[2][64 * kMaxC * 2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * kRowsPerBlock + wave;
+  const bool live = row < rows;
+  const int n8 = width >> 3;
+  const Tact* pa = ya + row * width;
+  const Tact* ps = ys + row * width;
+  float a[kMaxC][8], s[kMaxC][8];
+  if (live) {
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k) {
+      const int c = lane + 64 * k;
+      if (c < n8) {
+        Vec8<Tact>::ld(pa + 8 * c, a[k]);
+        Vec8<Tact>::ld(ps + 8 * c, s[k]);
+      }
+    }
+  }
+  for (int i = threadIdx.x; i < 2 * n8; i += 64 * kRowsPerBlock) {
+    sb[0][i] = ((const float4*)ba)[i];
+    sb[1][i] = ((const float4*)bs)[i];
+  }
+  __syncthreads();
+  if (!live) return;
+  float sa = 0.f, ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxC; ++k)
+    if (lane + 64 * k < n8)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sa += a[k][i] * a[k][i];
+        ss += s[k][i] * s[k][i];
+      }
+  sa = wave_sum(sa);
+  ss = wave_sum(ss);
+  const float ra = 0.5f / sqrtf(sa / (float)width + eps);
+  const float rs = 0.5f / sqrtf(ss / (float)width + eps);
+  Tact* po = out + row * width;
+#pragma unroll
+  for (int k = 0; k < kMaxC; ++k) {
+    const int c = lane + 64 * k;
+    if (c < n8) {
+      const float4 a0 = sb[0][2 * c], a1 = sb[0][2 * c + 1];
+      const float4 s0 = sb[1][2 * c], s1 = sb[1][2 * c + 1];
+      const float w1[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float w2[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      float r[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) r[i] = w1[i] * a[k][i] * ra + w2[i] * s[k][i] * rs;
+      Vec8<Tact>::st(po + 8 * c, r);
+    }
   }
 }
 
@@ -179,7 +197,12 @@ template <typename Tact>
 void launch_norm(const void* ya, const void* ys, const float* ba, const float* bs, float eps,
                  void* out, long long rows, int width, hipStream_t st) {
   const dim3 grid((unsigned)((rows + 3) / 4));
-  if (width % 8 == 0)
+  if (width % 8 == 0 && width <= 64 * 8 * kMaxC)
+    hipLaunchKernelGGL(norm_mean_rows<Tact>, dim3((unsigned)((rows + kRowsPerBlock - 1) /
+                                                            kRowsPerBlock)),
+                       dim3(64 * kRowsPerBlock), 0, st, (const Tact*)ya, (const Tact*)ys, ba, bs,
+                       eps, (Tact*)out, rows, width);
+  else if (width % 8 == 0)
     hipLaunchKernelGGL(norm_mean_vec<Tact>, grid, dim3(256), 0, st, (const Tact*)ya,
                        (const Tact*)ys, ba, bs, eps, (Tact*)out, rows, width);
   else

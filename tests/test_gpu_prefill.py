@@ -205,6 +205,43 @@ def test_mixer_prefill(shape):
     assert np.array_equal(down(r["conv_state"]), ref["conv_state"])
 
 
+# bf16 layers on one stream take the fused launch sequence (pre-pass | chunk
+# aggregates, attention | carry, final pass, norm): short sequences with a
+# single scan chunk, ragged lengths, several sequences, global attention
+@pytest.mark.parametrize("B,M,N,W,Hq,Hkv", [(1, 4, 20, 16, 5, 5), (1, 5, 77, 32, 4, 2),
+                                            (2, 16, 300, 64, 10, 5), (3, 0, 129, 0, 5, 1),
+                                            (1, 128, 1000, 1024, 25, 5)])
+def test_mixer_prefill_bf16_fused_shapes(B, M, N, W, Hq, Hkv):
+    shape = with_(SWA_PREFILL, B=B, M=M, N=N, W=W, Hq=Hq, Hkv=Hkv, Di=Hq * 64)
+    inp = prefill_inputs(shape, 21 + N)
+    t = up_inputs(inp, "bf16")
+    r = hm.mixer_prefill(t, shape.M, shape.W)
+    torch.cuda.synchronize()
+    ref = oracle.mixer_prefill(inp, shape.M, shape.W)
+    for k in ("ya", "ys", "out", "ssm_state"):
+        assert_close(down(r[k]), ref[k], "bf16", f"mixer {k}")
+    assert np.array_equal(down(r["conv_state"]), ref["conv_state"])
+
+
+def test_mixer_prefill_kv_reuse_one_stream():
+    shape = with_(SWA_PREFILL, N=400, M=32, W=128)
+    prod, cons = prefill_inputs(shape, 14), prefill_inputs(shape, 15)
+    tp, tc = up_inputs(prod, "bf16"), up_inputs(cons, "bf16")
+    del tc["k"], tc["v"]
+    tc["Hkv"] = shape.Hkv
+    p1 = hm.PrefillPlan(tp, shape.M, shape.W)
+    p2 = hm.PrefillPlan(tc, shape.M, shape.W, kv=p1.kv, kv_reuse=True)
+    p1.run()
+    p2.run()
+    torch.cuda.synchronize()
+    mixed = dict(cons)
+    mixed["k"], mixed["v"] = prod["k"], prod["v"]
+    for plan, src in ((p1, prod), (p2, mixed)):
+        ref = oracle.mixer_prefill(src, shape.M, shape.W)
+        for k, got in (("ya", plan.ya), ("ys", plan.ys), ("out", plan.out)):
+            assert_close(down(got), ref[k], "bf16", k)
+
+
 # ------------------------------------------------------------------ prepared K/V, two streams
 def test_prepared_kv_shared_between_layers():
     shape = with_(SWA_PREFILL, N=500, M=16, W=128)
