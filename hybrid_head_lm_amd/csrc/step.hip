@@ -43,13 +43,15 @@ HM_DEV float ldx(const Tact* p) { return ActIO<Tact>::ld(p); }
 // ---------------------------------------------------------------- per-sequence combine
 // One workgroup of kCombThreads per sequence b.  Part layout per sequence:
 // [Hkv][n_split][grp][Dh + 2] = (max in log2 units, sum, unnormalised O[Dh]).
-//   1) every (head, split) max / sum to LDS (one round of loads);
-//   2) per head the merge weights w[h][s] = exp2(m_s - M) / sum_s' exp2(m_s' - M) l_s';
-//   3) Y_attn[h, d] = sum_s w[h][s] O_s[h, d] (all loads of a thread issued together),
-//      then out = 0.5 (beta_a Y_attn / rms + beta_s Y_ssm / rms).
+// Every load is issued up front (one round trip to memory): the (max, sum) of
+// every (head, split) go to LDS, and each thread holds the split partials of
+// its outputs.  Then per output Y_attn[h, d] = sum_s w_s O_s[h, d] with
+// w_s = exp2(m_s - M) / sum_s' exp2(m_s' - M) l_s', and
+// out = 0.5 (beta_a Y_attn / rms(Y_attn) + beta_s Y_ssm / rms(Y_ssm)).
 constexpr int kCombThreads = 512;
 constexpr int kCombMaxW = 2048;      // Hq * n_split entries held in LDS
 constexpr int kCombPer = 8;          // outputs per thread (Di <= 4096)
+constexpr int kCombMaxSplit = 8;     // split partials held in registers per output (more: re-read)
 
 template <typename Tact>
 __global__ __launch_bounds__(kCombThreads) void step_combine(
@@ -57,48 +59,68 @@ __global__ __launch_bounds__(kCombThreads) void step_combine(
     size_t ys_stride, const float* __restrict__ ba, const float* __restrict__ bs, float eps,
     Tact* __restrict__ out, float* __restrict__ ya_out, float* __restrict__ ys_out, int Hq,
     int Hkv, int Dh, int n_split, int Di) {
-  __shared__ float sw[kCombMaxW];
+  __shared__ float sm[kCombMaxW], sl[kCombMaxW];
   __shared__ float red[2][kCombThreads / 64];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int grp = Hq / Hkv, stride = Dh + 2;
   const float* pb = part + (size_t)b * part_b_stride;
   const float* yb = ys_ws + (size_t)b * ys_stride;
-  // 1) + 2): entry e = h * n_split + s
+  // (max, sum) of entry e = h * n_split + s
   for (int e = tid; e < Hq * n_split; e += kCombThreads) {
-    const int h = e / n_split, s = e % n_split;
+    const int h = e / n_split, sp = e % n_split;
     const int g = h / grp, hh = h % grp;
-    sw[e] = pb[(((size_t)g * n_split + s) * grp + hh) * stride];            // max
+    const float* ph = pb + (((size_t)g * n_split + sp) * grp + hh) * stride;
+    sm[e] = ph[0];
+    sl[e] = ph[1];
+  }
+  // this thread's outputs: split partials, SSM branch, betas
+  float o[kCombPer][kCombMaxSplit], yv[kCombPer], wa[kCombPer], wsv[kCombPer];
+#pragma unroll
+  for (int k = 0; k < kCombPer; ++k) {
+    const int idx = tid + k * kCombThreads;
+    if (idx < Di) {
+      const int h = idx / Dh, d = idx % Dh;
+      const int g = h / grp, hh = h % grp;
+      const float* base = pb + ((size_t)g * n_split * grp + hh) * stride + 2 + d;
+#pragma unroll
+      for (int sp = 0; sp < kCombMaxSplit; ++sp)
+        o[k][sp] = sp < n_split ? base[(size_t)sp * grp * stride] : 0.f;
+      yv[k] = yb[idx];
+      wa[k] = ba[idx];
+      wsv[k] = bs[idx];
+    }
   }
   __syncthreads();
-  const bool owner = tid < Hq;   // one thread per head turns maxima into weights
-  if (owner) {
-    const int h = tid, g = h / grp, hh = h % grp;
-    float M = sw[h * n_split];
-    for (int s = 1; s < n_split; ++s) M = fmaxf(M, sw[h * n_split + s]);
-    float L = 0.f;
-    for (int s = 0; s < n_split; ++s)
-      L += fast_exp2(sw[h * n_split + s] - M) * pb[(((size_t)g * n_split + s) * grp + hh) * stride + 1];
-    const float inv = 1.f / L;
-    for (int s = 0; s < n_split; ++s) sw[h * n_split + s] = fast_exp2(sw[h * n_split + s] - M) * inv;
-  }
-  __syncthreads();
-  // 3)
-  float ya[kCombPer], yv[kCombPer];
+  float ya[kCombPer];
   float sa = 0.f, ss = 0.f;
 #pragma unroll
   for (int k = 0; k < kCombPer; ++k) {
     const int idx = tid + k * kCombThreads;
     ya[k] = 0.f;
-    yv[k] = 0.f;
     if (idx < Di) {
       const int h = idx / Dh, d = idx % Dh;
+      const float* mh = sm + h * n_split;
+      const float* lh = sl + h * n_split;
+      float M = mh[0];
+      for (int sp = 1; sp < n_split; ++sp) M = fmaxf(M, mh[sp]);
+      float L = 0.f, acc = 0.f;
+#pragma unroll
+      for (int sp = 0; sp < kCombMaxSplit; ++sp)
+        if (sp < n_split) {
+          const float w = fast_exp2(mh[sp] - M);
+          L += w * lh[sp];
+          acc += w * o[k][sp];
+        }
+      // splits beyond those held in registers (long global caches)
       const int g = h / grp, hh = h % grp;
       const float* base = pb + ((size_t)g * n_split * grp + hh) * stride + 2 + d;
-      float acc = 0.f;
-      for (int s = 0; s < n_split; ++s) acc += sw[h * n_split + s] * base[(size_t)s * grp * stride];
-      ya[k] = acc;
-      yv[k] = yb[idx];
-      sa += acc * acc;
+      for (int sp = kCombMaxSplit; sp < n_split; ++sp) {
+        const float w = fast_exp2(mh[sp] - M);
+        L += w * lh[sp];
+        acc += w * base[(size_t)sp * grp * stride];
+      }
+      ya[k] = acc / L;
+      sa += ya[k] * ya[k];
       ss += yv[k] * yv[k];
     }
   }
@@ -125,7 +147,7 @@ __global__ __launch_bounds__(kCombThreads) void step_combine(
   for (int k = 0; k < kCombPer; ++k) {
     const int idx = tid + k * kCombThreads;
     if (idx < Di) {
-      ActIO<Tact>::st(out + (size_t)b * Di + idx, ba[idx] * ya[k] * ra + bs[idx] * yv[k] * rs);
+      ActIO<Tact>::st(out + (size_t)b * Di + idx, wa[k] * ya[k] * ra + wsv[k] * yv[k] * rs);
       if (ya_out) ya_out[(size_t)b * Di + idx] = ya[k];
       if (ys_out) ys_out[(size_t)b * Di + idx] = yv[k];
     }
@@ -185,10 +207,12 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
     const float* __restrict__ D, const float* __restrict__ cw, const float* __restrict__ cb,
     float* __restrict__ conv_state, float* __restrict__ ssm_state, float* __restrict__ ys_ws, size_t ys_stride, float* __restrict__ part, size_t part_b_stride,
     int Hq, int Hkv, int Di, int S, int L, int slot, long long pos, float qscale,
-    double log2_base, int n_split, int n_attn, int ssm_per_b) {
+    double log2_base, double rstep, int n_split, int n_attn, int ssm_per_b) {
   __shared__ __attribute__((aligned(16))) bf16_t sVt[4][64 * kVRow];
   __shared__ float sm[4][16], sl[4][16];
-  __shared__ float sO[4][16][64];
+  // a wave's unnormalised O (16 heads x 64 dims, float) reuses its own V^T tile
+  // once the PV product has consumed it
+  static_assert(16 * 64 * sizeof(float) <= 64 * kVRow * sizeof(bf16_t), "O fits the V^T tile");
   const int tid = threadIdx.x;
   const int grp = Hq / Hkv;
   if ((int)blockIdx.x < n_attn) {
@@ -224,10 +248,18 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
       const bf16_t* p0 = (const bf16_t*)&r0;
       const bf16_t* p1 = (const bf16_t*)&r1;
       const float qs = n < grp ? qscale : 0.f;
+      // theta_d / 2 pi = rstep^d / 2 pi for d = 8G..8G+7 by double-precision products
+      const double s2 = rstep * rstep, s4 = s2 * s2, s8 = s4 * s4;
+      double th = 0.15915494309189533576888376337251;
+      for (int gg = 0; gg < G; ++gg) th *= s8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float sn, cs;
-        rope_sincos(pos, 8 * G + e, 64, log2_base, &sn, &cs);
+        double r = (double)pos * th;
+        r -= rint(r);
+        sn = __builtin_amdgcn_sinf((float)r);
+        cs = __builtin_amdgcn_cosf((float)r);
+        th *= rstep;
         const float x1 = bf2f(p0[e]), x2 = bf2f(p1[e]);
         qf[0][e] = (__bf16)((x1 * cs - x2 * sn) * qs);
         qf[1][e] = (__bf16)((x2 * cs + x1 * sn) * qs);
@@ -313,10 +345,14 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
       sm[wave][n] = m_run;
       sl[wave][n] = l_run;
     }
+    float* sOw = (float*)&sVt[wave][0];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sO[wave][n][16 * db + 4 * G + i] = acc[db][i];
+      for (int i = 0; i < 4; ++i) sOw[n * 64 + 16 * db + 4 * G + i] = acc[db][i];
     __syncthreads();
     float* dst = part + (size_t)b * part_b_stride + ((size_t)g * n_split + split) * grp * 66;
     for (int idx = tid; idx < grp * 64; idx += 256) {
@@ -329,7 +365,7 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
       for (int w = 0; w < 4; ++w) {
         const float f = fast_exp2(sm[w][hh] - M);
         Ls += sl[w][hh] * f;
-        O += sO[w][hh][d] * f;
+        O += ((const float*)&sVt[w][0])[hh * 64 + d] * f;
       }
       float* ph = dst + hh * 66;
       if (d == 0) {
@@ -544,7 +580,8 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
                        (const bf16_t*)a->delta, (const bf16_t*)a->Bm, (const bf16_t*)a->Cm,
                        (const bf16_t*)a->z, a->A, a->D, a->conv_w, a->conv_b, a->conv_state,
                        a->ssm_state, ys_ws, g.ys_stride, part, g.part_b_stride, a->Hq, a->Hkv,
-                       a->Di, S, g.L, slot, pos, sc, l2b, g.n_split, n_attn, ssm_per_b);
+                       a->Di, S, g.L, slot, pos, sc, l2b, exp2(-l2b / 32.0), g.n_split,
+                       n_attn, ssm_per_b);
     hm_status s = hm::check_launch("step_fused_bf16");
     if (s != HM_OK) return s;
     hipLaunchKernelGGL(step_combine<bf16_t>, dim3(a->B), dim3(kCombThreads), 0, st,

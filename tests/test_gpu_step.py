@@ -76,6 +76,13 @@ def test_decode_pair_bf16_global(n_prev):
     _check(shape, 11 + n_prev)
 
 
+def test_decode_pair_bf16_global_long_cache():
+    """A global layer with a long cache: more key splits than the combine keeps
+    in registers."""
+    shape = with_(DECODE_PAIR, B=2, W=0, cache_slots=4096, n_prev=3000, M=64)
+    _check(shape, 17)
+
+
 @pytest.mark.parametrize("n_prev", [0, 5, 15, 16, 40])
 @pytest.mark.parametrize("Dh", [16, 64])
 def test_decode_pair_f32(n_prev, Dh):
