@@ -22,6 +22,8 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs (no AGPR copies around every MFMA)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I", os.path.join(HERE, "..", "include"),
 ]

@@ -10,23 +10,14 @@
 // With one n_prev for the batch the visible rows are exactly the contiguous
 // range [0, M + min(n_prev+1, W)).
 //
-// bf16 path: step_fused_bf16 holds two kinds of blocks:
-//   attention blocks  split over keys: a workgroup of 4 waves covers 256 cache
-//                     rows of one (b, kv group); each wave takes 64 rows,
-//                     computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (the
-//                     group's query heads on the 16 MFMA columns, K straight
-//                     from HBM as the A operand), a softmax, and O^T = V^T P^T
-//                     with V^T staged through LDS; the 4 waves merge in LDS and
-//                     write one partial (max, sum, unnormalised O) per head.
-//                     The block whose rows hold the new token's slot (producer
-//                     layer) first rotates k_new and writes k_new / v_new there.
-//   SSM blocks        conv step + one scan step per (b, channel), in place on
-//                     the states; branch output to the workspace.
-// then step_combine (one workgroup per sequence) merges the partials into
+// bf16 path: step_fused_bf16, one workgroup per (sequence, kv group, key split)
+// that streams its K/V tiles through LDS and also runs a share of the SSM step,
+// then step_combine (one workgroup per sequence) merges the key splits into
 // Y_attn and applies the branch RMS norm, rescale and average: two launches
 // per layer.
 // float32 path (Dh in {16, 32, 64}): SSM step + KV write, one thread per
 // (b, head) over all visible rows, then the same combine kernel.
+#include <algorithm>
 #include <cmath>
 
 #include "hm_common.h"
@@ -34,8 +25,6 @@
 namespace {
 
 constexpr int kNS = 16;
-constexpr int kKeysPerWG = 256;
-constexpr int kVRow = 72;  // padded LDS row of the transposed V tile (bf16 elements)
 
 template <typename Tact>
 HM_DEV float ldx(const Tact* p) { return ActIO<Tact>::ld(p); }
@@ -196,191 +185,304 @@ HM_DEV float ssm_step_one(int b, int c, int Di, const Tact* __restrict__ x,
 }
 
 // ---------------------------------------------------------------- bf16 attention + SSM step
-// Blocks [0, n_attn) are (sequence, kv group, key split) attention blocks; the
-// rest are SSM-step blocks of 256 channels.  The per-sequence merge runs in the
-// next launch (step_combine), so no block depends on another.
+// LDS tiles of 64 cache rows x 128 bytes (K or V); the 16-byte chunk c of row r
+// sits in slot c ^ ((r >> 1) & 7), so that 16 lanes reading one chunk of 16
+// consecutive rows hit 16 different bank groups of the 64-bank LDS.
+HM_DEV int dec_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
+HM_DEV int dec_off(int row, int c) { return row * 128 + (dec_slot(row, c) << 4); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4_v __attribute__((ext_vector_type(4)));
+
+constexpr int kDecStages = 3;   // 64-row K/V tiles in flight per workgroup (48 KB)
+
+// One workgroup of 4 waves per (sequence b, kv head g, key split).  The split's
+// 64-row tiles of K and V stream HBM -> LDS with global_load_lds through a
+// 3-stage ring; wave w takes rows 16w..16w+15 of every tile: S^T = K Q^T with
+// v_mfma_f32_16x16x32_bf16 (the group's query heads on the 16 columns), an
+// online softmax per head, and O^T += V^T P^T with v_mfma_f32_16x16x16_bf16
+// (V^T read from the row-major tile).  The 4 waves merge in LDS and write one
+// partial (max, sum, unnormalised O) per head; step_combine merges the splits.
+// While its first tiles load, the workgroup also runs its share of the SSM
+// step (conv step + one scan step per (b, channel), in place on the states).
+// The workgroup whose rows hold the new token's slot (producer layer) first
+// rotates k_new and writes k_new / v_new there.
 __global__ __launch_bounds__(256) void step_fused_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_new,
     const bf16_t* __restrict__ v_new, bf16_t* __restrict__ kc, bf16_t* __restrict__ vc,
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ dl, const bf16_t* __restrict__ Bm,
     const bf16_t* __restrict__ Cm, const bf16_t* __restrict__ z, const float* __restrict__ A,
     const float* __restrict__ D, const float* __restrict__ cw, const float* __restrict__ cb,
-    float* __restrict__ conv_state, float* __restrict__ ssm_state, float* __restrict__ ys_ws, size_t ys_stride, float* __restrict__ part, size_t part_b_stride,
-    int Hq, int Hkv, int Di, int S, int L, int slot, long long pos, float qscale,
-    double log2_base, double rstep, int n_split, int n_attn, int ssm_per_b) {
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[4][64 * kVRow];
+    float* __restrict__ conv_state, float* __restrict__ ssm_state, float* __restrict__ ys_ws,
+    size_t ys_stride, float* __restrict__ part, size_t part_b_stride, int Hq, int Hkv, int Di,
+    int S, int L, int slot, long long pos, float qscale, double log2_base, double rstep,
+    int n_split, int tiles_per_split, int ssm_per_block, int n_ssm) {
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecStages][2][8192];
   __shared__ float sm[4][16], sl[4][16];
-  // a wave's unnormalised O (16 heads x 64 dims, float) reuses its own V^T tile
-  // once the PV product has consumed it
-  static_assert(16 * 64 * sizeof(float) <= 64 * kVRow * sizeof(bf16_t), "O fits the V^T tile");
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, G = lane >> 4;
   const int grp = Hq / Hkv;
-  if ((int)blockIdx.x < n_attn) {
-    const int split = blockIdx.x % n_split, pair = blockIdx.x / n_split;
-    const int b = pair / Hkv;
-    const int g = pair % Hkv;
-    const size_t rs = (size_t)Hkv * 64;                   // cache row stride (elements)
-    if (k_new != nullptr && slot >= split * kKeysPerWG && slot < (split + 1) * kKeysPerWG) {
-      // the new token's row lies in this block's key range: write it first
-      if (tid < 32) {
-        const bf16_t* ks = k_new + ((size_t)b * Hkv + g) * 64;
-        const bf16_t* vs = v_new + ((size_t)b * Hkv + g) * 64;
-        float sn, cs;
-        rope_sincos(pos, tid, 64, log2_base, &sn, &cs);
-        const float x1 = bf2f(ks[tid]), x2 = bf2f(ks[tid + 32]);
-        const size_t off = ((size_t)b * S + slot) * rs + (size_t)g * 64;
-        kc[off + tid] = f2bf(x1 * cs - x2 * sn);
-        kc[off + tid + 32] = f2bf(x2 * cs + x1 * sn);
-        vc[off + tid] = vs[tid];
-        vc[off + tid + 32] = vs[tid + 32];
-      }
-      __threadfence_block();
+  const int split = blockIdx.x % n_split, pair = blockIdx.x / n_split;
+  const int b = pair / Hkv, g = pair % Hkv;
+  const size_t rs = (size_t)Hkv * 64;                       // cache row stride (elements)
+  const int kt0 = split * tiles_per_split;                  // first tile of the split
+  const int ntile = max(0, min(tiles_per_split, (L + 63) / 64 - kt0));
+
+  // 1) producer: the new token's row first, if it lies in this split
+  if (k_new != nullptr && slot >= kt0 * 64 && slot < (kt0 + ntile) * 64) {
+    if (tid < 32) {
+      const bf16_t* ks = k_new + ((size_t)b * Hkv + g) * 64;
+      const bf16_t* vs = v_new + ((size_t)b * Hkv + g) * 64;
+      float sn, cs;
+      rope_sincos(pos, tid, 64, log2_base, &sn, &cs);
+      const float x1 = bf2f(ks[tid]), x2 = bf2f(ks[tid + 32]);
+      const size_t off = ((size_t)b * S + slot) * rs + (size_t)g * 64;
+      kc[off + tid] = f2bf(x1 * cs - x2 * sn);
+      kc[off + tid + 32] = f2bf(x2 * cs + x1 * sn);
+      vc[off + tid] = vs[tid];
+      vc[off + tid + 32] = vs[tid + 32];
+    }
+    __threadfence_block();
+    __syncthreads();
+  }
+
+  // 2) this workgroup's share of the SSM step, loads first: the first item of
+  // each thread is loaded now and computed after the attention loop, so the
+  // loads overlap the K/V stream (items past the first 256 run at the end)
+  const int sidx0 = blockIdx.x * ssm_per_block + tid;
+  const bool has_ssm = tid < ssm_per_block && sidx0 < n_ssm;
+  float4 sh[4], sa4[4], scw;
+  uint4 sbr[2], scr[2];
+  float ss0 = 0.f, ss1 = 0.f, ss2 = 0.f, sxv = 0.f, sdv = 0.f, szv = 0.f, sD = 0.f, scb = 0.f;
+  int sbq = 0, scq = 0;
+  if (has_ssm) {
+    sbq = sidx0 / Di;
+    scq = sidx0 % Di;
+    const size_t idx = (size_t)sbq * Di + scq;
+    const float* cs = conv_state + idx * 3;
+    ss0 = cs[0];
+    ss1 = cs[1];
+    ss2 = cs[2];
+    sxv = bf2f(x[idx]);
+    sdv = bf2f(dl[idx]);
+    szv = bf2f(z[idx]);
+    sD = D[scq];
+    scb = cb[scq];
+    scw = *(const float4*)(cw + (size_t)scq * 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sh[i] = ((const float4*)(ssm_state + idx * kNS))[i];
+      sa4[i] = ((const float4*)(A + (size_t)scq * kNS))[i];
+    }
+    sbr[0] = *(const uint4*)(Bm + (size_t)sbq * kNS);
+    sbr[1] = *(const uint4*)(Bm + (size_t)sbq * kNS + 8);
+    scr[0] = *(const uint4*)(Cm + (size_t)sbq * kNS);
+    scr[1] = *(const uint4*)(Cm + (size_t)sbq * kNS + 8);
+  }
+
+  // 3) the first two tiles: thread -> LDS rows 16 wave + 8 i + lane / 8, slot
+  // lane & 7 (global_load_lds writes lane L of a wave at base + 16 L)
+  const bf16_t* kb0 = kc + (size_t)b * S * rs + (size_t)g * 64;
+  const bf16_t* vb0 = vc + (size_t)b * S * rs + (size_t)g * 64;
+  int roff[2], coff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    roff[i] = 16 * wave + 8 * i + (lane >> 3);
+    coff[i] = dec_slot(roff[i], lane & 7) * 8;   // the slot map is an involution
+  }
+  auto issue = [&](int t) {
+    unsigned char* st = ring[t % kDecStages][0];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int key = min((kt0 + t) * 64 + roff[i], S - 1);   // rows past the cache: unused
+      __builtin_amdgcn_global_load_lds((const void*)(kb0 + (size_t)key * rs + coff[i]),
+                                       (lds_void_t*)(st + (16 * wave + 8 * i) * 128), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vb0 + (size_t)key * rs + coff[i]),
+                                       (lds_void_t*)(st + 8192 + (16 * wave + 8 * i) * 128), 16,
+                                       0, 0);
+    }
+  };
+  if (ntile > 0) issue(0);
+  if (ntile > 1) issue(1);
+
+  // 4) Q^T fragment (B operand): lane holds head n of the group, dims 8G+e and 32+8G+e
+  bf16x8_v qf[2];
+  {
+    const bf16_t* src = q + ((size_t)b * Hq + g * grp + min(n, grp - 1)) * 64;
+    const uint4 r0 = *(const uint4*)(src + 8 * G);
+    const uint4 r1 = *(const uint4*)(src + 32 + 8 * G);
+    const bf16_t* p0 = (const bf16_t*)&r0;
+    const bf16_t* p1 = (const bf16_t*)&r1;
+    const float qs = n < grp ? qscale : 0.f;
+    // theta_d / 2 pi = rstep^d / 2 pi for d = 8G..8G+7 by double-precision products
+    const double s2 = rstep * rstep, s4 = s2 * s2, s8 = s4 * s4;
+    double th = 0.15915494309189533576888376337251;
+    for (int gg = 0; gg < G; ++gg) th *= s8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      double r = (double)pos * th;
+      r -= rint(r);
+      const float sn = __builtin_amdgcn_sinf((float)r), cs = __builtin_amdgcn_cosf((float)r);
+      th *= rstep;
+      const float x1 = bf2f(p0[e]), x2 = bf2f(p1[e]);
+      qf[0][e] = (__bf16)((x1 * cs - x2 * sn) * qs);
+      qf[1][e] = (__bf16)((x2 * cs + x1 * sn) * qs);
+    }
+  }
+
+  // 5) stream the tiles; per lane: head n, keys 16 wave + 4G + i of each tile
+  const float NEG_INF = -__builtin_huge_valf();
+  float m_run = -1e30f, l_run = 0.f;
+  f32x4_v acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[db][i] = 0.f;
+  const int krow = 16 * wave + n;            // A-operand row of this lane (K)
+  // V^T operand offsets in a tile: dim 16 db + n, rows 16 wave + 4G + e
+  int voff[4][4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = 16 * db + n, row = 16 * wave + 4 * G + e;
+      voff[db][e] = dec_off(row, d >> 3) + (d & 7) * 2;
+    }
+  // The loop is unrolled by the ring depth so that every LDS address is a
+  // register plus an immediate.
+  for (int t0 = 0; t0 < ntile; t0 += kDecStages) {
+#pragma unroll
+    for (int u = 0; u < kDecStages; ++u) {
+      const int t = t0 + u;
+      if (t >= ntile) break;
+      if (t == 0 || t + 1 >= ntile) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));   // tile t+1 may stay in flight
       __syncthreads();
-    }
-    const int lane = tid & 63, wave = tid >> 6;
-    const int n = lane & 15, G = lane >> 4;
-    // Q^T fragment (B operand): lane holds head n of the group, dims 8G+e and 32+8G+e.
-    bf16x8_v qf[2];
-    {
-      const bf16_t* src = q + ((size_t)b * Hq + g * grp + min(n, grp - 1)) * 64;
-      const uint4 r0 = *(const uint4*)(src + 8 * G);
-      const uint4 r1 = *(const uint4*)(src + 32 + 8 * G);
-      const bf16_t* p0 = (const bf16_t*)&r0;
-      const bf16_t* p1 = (const bf16_t*)&r1;
-      const float qs = n < grp ? qscale : 0.f;
-      // theta_d / 2 pi = rstep^d / 2 pi for d = 8G..8G+7 by double-precision products
-      const double s2 = rstep * rstep, s4 = s2 * s2, s8 = s4 * s4;
-      double th = 0.15915494309189533576888376337251;
-      for (int gg = 0; gg < G; ++gg) th *= s8;
+      if (t + 2 < ntile) issue(t + 2);
+      const unsigned char* sk = ring[u][0];
+      const unsigned char* sv = ring[u][1];
+      f32x4_v sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float sn, cs;
-        double r = (double)pos * th;
-        r -= rint(r);
-        sn = __builtin_amdgcn_sinf((float)r);
-        cs = __builtin_amdgcn_cosf((float)r);
-        th *= rstep;
-        const float x1 = bf2f(p0[e]), x2 = bf2f(p1[e]);
-        qf[0][e] = (__bf16)((x1 * cs - x2 * sn) * qs);
-        qf[1][e] = (__bf16)((x2 * cs + x1 * sn) * qs);
-      }
-    }
-    const int j0 = (split * 4 + wave) * 64;
-    float m_run = -1e30f, l_run = 0.f;
-    f32x4_v acc[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[db][i] = 0.f;
-    if (j0 < L) {
-      const bf16_t* kbase = kc + ((size_t)b * S) * rs + (size_t)g * 64;
-      const bf16_t* vbase = vc + ((size_t)b * S) * rs + (size_t)g * 64;
-      // All 16 loads of the tile are unconditional (rows past L are clamped and
-      // masked afterwards), so they are all in flight together.
-      bf16x8_v kf[4][2];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int key = min(j0 + 32 * (kb >> 1) + 8 * (n >> 2) + 4 * (kb & 1) + (n & 3), L - 1);
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          kf[kb][s] = *(const bf16x8_v*)(kbase + (size_t)key * rs + 32 * s + 8 * G);
-      }
-      uint4 vr[8];
-      {
-        const int key = min(j0 + lane, L - 1);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) vr[r] = *(const uint4*)(vbase + (size_t)key * rs + 8 * r);
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const bf16_t* pv = (const bf16_t*)&vr[r];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sVt[wave][(8 * r + e) * kVRow + lane] = pv[e];
-      }
-      f32x4_v sc[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[kb][i] = 0.f;
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][s], qf[s], sc[kb], 0, 0, 0);
-      }
-      const float NEG_INF = -__builtin_huge_valf();
+      for (int s = 0; s < 2; ++s)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            *(const bf16x8_v*)(sk + dec_off(krow, G + 4 * s)), qf[s], sc, 0, 0, 0);
+      const int kbase = (kt0 + t) * 64 + 16 * wave + 4 * G;
       float mx = NEG_INF;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = j0 + 32 * (kb >> 1) + 8 * G + 4 * (kb & 1) + i;
-          if (key >= L) sc[kb][i] = NEG_INF;
-          mx = fmaxf(mx, sc[kb][i]);
-        }
+      for (int i = 0; i < 4; ++i) {
+        if (kbase + i >= L) sc[i] = NEG_INF;
+        mx = fmaxf(mx, sc[i]);
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      m_run = mx;
-      bf16x8_v pf[2];
+      // lazily moved reference: O and l are rescaled only when a tile's maximum
+      // exceeds the running reference by more than 8 (log2 units)
+      if (__ballot(mx > m_run + 8.f) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = fast_exp2(sc[kb][i] - mx);
-          l_run += p;
-          pf[kb >> 1][4 * (kb & 1) + i] = (__bf16)p;
-        }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8_v a = *(const bf16x8_v*)(&sVt[wave][(16 * db + n) * kVRow + 32 * s + 8 * G]);
-          acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[s], acc[db], 0, 0, 0);
-        }
-    }
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (G == 0) {
-      sm[wave][n] = m_run;
-      sl[wave][n] = l_run;
-    }
-    float* sOw = (float*)&sVt[wave][0];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sOw[n * 64 + 16 * db + 4 * G + i] = acc[db][i];
-    __syncthreads();
-    float* dst = part + (size_t)b * part_b_stride + ((size_t)g * n_split + split) * grp * 66;
-    for (int idx = tid; idx < grp * 64; idx += 256) {
-      const int hh = idx >> 6, d = idx & 63;
-      float M = sm[0][hh];
-#pragma unroll
-      for (int w = 1; w < 4; ++w) M = fmaxf(M, sm[w][hh]);
-      float Ls = 0.f, O = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = fast_exp2(sm[w][hh] - M);
-        Ls += sl[w][hh] * f;
-        O += ((const float*)&sVt[w][0])[hh * 64 + d] * f;
+          for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
       }
-      float* ph = dst + hh * 66;
-      if (d == 0) {
-        ph[0] = M;
-        ph[1] = Ls;
+      s16x4_v pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(sc[i] - m_run);
+        l_run += p;
+        pb[i] = (short)f2bf(p);
       }
-      ph[2 + d] = O;
+      // V^T operand: lane holds dim 16 db + n, keys 16 wave + 4G + e (e = 0..3)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        s16x4_v va;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) va[e] = *(const short*)(sv + voff[db][e]);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[db], 0, 0, 0);
+      }
     }
-  } else {
-    const int sb = blockIdx.x - n_attn;
-    const int b = sb / ssm_per_b;
-    const int c = (sb % ssm_per_b) * 256 + tid;
-    if (c < Di)
-      ys_ws[(size_t)b * ys_stride + c] =
-          ssm_step_one<bf16_t>(b, c, Di, x, dl, Bm, Cm, z, A, D, cw, cb, conv_state, ssm_state);
+  }
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  // 6) the SSM step of this workgroup's items (conv step, scan step, gate)
+  if (has_ssm) {
+    const size_t idx = (size_t)sbq * Di + scq;
+    const float u = scb + scw.x * ss0 + scw.y * ss1 + scw.z * ss2 + scw.w * sxv;
+    float* cs = conv_state + idx * 3;
+    cs[0] = ss1;
+    cs[1] = ss2;
+    cs[2] = sxv;
+    const float xc = siluf_(u);
+    const float du = sdv * xc;
+    const float hv[kNS] = {sh[0].x, sh[0].y, sh[0].z, sh[0].w, sh[1].x, sh[1].y, sh[1].z, sh[1].w,
+                           sh[2].x, sh[2].y, sh[2].z, sh[2].w, sh[3].x, sh[3].y, sh[3].z, sh[3].w};
+    const float av[kNS] = {sa4[0].x, sa4[0].y, sa4[0].z, sa4[0].w, sa4[1].x, sa4[1].y,
+                           sa4[1].z, sa4[1].w, sa4[2].x, sa4[2].y, sa4[2].z, sa4[2].w,
+                           sa4[3].x, sa4[3].y, sa4[3].z, sa4[3].w};
+    const uint32_t bw[8] = {sbr[0].x, sbr[0].y, sbr[0].z, sbr[0].w,
+                            sbr[1].x, sbr[1].y, sbr[1].z, sbr[1].w};
+    const uint32_t cwd[8] = {scr[0].x, scr[0].y, scr[0].z, scr[0].w,
+                             scr[1].x, scr[1].y, scr[1].z, scr[1].w};
+    float hn[kNS];
+    float y4[4] = {sD * xc, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nn = 0; nn < kNS; ++nn) {
+      const uint32_t wb = bw[nn >> 1], wc = cwd[nn >> 1];
+      const float bv = __uint_as_float((nn & 1) ? (wb & 0xffff0000u) : (wb << 16));
+      const float cv = __uint_as_float((nn & 1) ? (wc & 0xffff0000u) : (wc << 16));
+      hn[nn] = fast_exp2(sdv * (av[nn] * kLog2e)) * hv[nn] + du * bv;
+      y4[nn & 3] += cv * hn[nn];
+    }
+    float4* hs = (float4*)(ssm_state + idx * kNS);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      hs[i] = make_float4(hn[4 * i], hn[4 * i + 1], hn[4 * i + 2], hn[4 * i + 3]);
+    ys_ws[(size_t)sbq * ys_stride + scq] = ((y4[0] + y4[1]) + (y4[2] + y4[3])) * siluf_(szv);
+  }
+  for (int j = tid + 256; j < ssm_per_block; j += 256) {
+    const int sidx = blockIdx.x * ssm_per_block + j;
+    if (sidx < n_ssm) {
+      const int bs = sidx / Di, c = sidx % Di;
+      ys_ws[(size_t)bs * ys_stride + c] =
+          ssm_step_one<bf16_t>(bs, c, Di, x, dl, Bm, Cm, z, A, D, cw, cb, conv_state, ssm_state);
+    }
+  }
+
+  // 7) merge the 4 waves: (max, sum) per head and O^T (dims 16 db + 4G + i, head n)
+  __syncthreads();                                  // every wave is done with the ring
+  float* sO = (float*)&ring[0][0][0];               // [wave][head 16][dim 64]
+  if (G == 0) {
+    sm[wave][n] = m_run;
+    sl[wave][n] = l_run;
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sO[(wave * 16 + n) * 64 + 16 * db + 4 * G + i] = acc[db][i];
+  __syncthreads();
+  float* dst = part + (size_t)b * part_b_stride + ((size_t)g * n_split + split) * grp * 66;
+  for (int idx = tid; idx < grp * 64; idx += 256) {
+    const int hh = idx >> 6, d = idx & 63;
+    float M = sm[0][hh];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm[w][hh]);
+    float Ls = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float f = fast_exp2(sm[w][hh] - M);
+      Ls += sl[w][hh] * f;
+      O += sO[(w * 16 + hh) * 64 + d] * f;
+    }
+    float* ph = dst + hh * 66;
+    if (d == 0) {
+      ph[0] = M;
+      ph[1] = Ls;
+    }
+    ph[2 + d] = O;
   }
 }
 
@@ -468,10 +570,14 @@ __global__ __launch_bounds__(256) void step_ssm_kv(
 }
 
 struct StepGeom {
-  int L, n_split, grp;
+  int L, n_split, tiles_per_split, grp;
   size_t ys_stride, part_b_stride;            // floats per sequence
   size_t ys_bytes, part_bytes;
 };
+
+// bf16 decode: key splits of whole 64-row tiles, about kDecBlocks workgroups
+// in all (two to three per CU stream at once with 48 KB of LDS each).
+constexpr int kDecBlocks = 640;
 
 StepGeom step_geom(const hm_step_args* a) {
   StepGeom s{};
@@ -479,7 +585,15 @@ StepGeom step_geom(const hm_step_args* a) {
                                      : a->n_prev + 1;
   s.L = (int)(a->n_meta + nv);
   s.grp = a->Hkv > 0 ? a->Hq / a->Hkv : 0;
-  s.n_split = a->dtype == HM_BF16 ? (s.L + kKeysPerWG - 1) / kKeysPerWG : 1;
+  s.n_split = 1;
+  s.tiles_per_split = 1;
+  if (a->dtype == HM_BF16) {
+    const int nt = (s.L + 63) / 64;
+    const long long pairs = (long long)a->B * a->Hkv;
+    const int want = (int)std::max(1LL, std::min<long long>(nt, (kDecBlocks + pairs - 1) / pairs));
+    s.tiles_per_split = (nt + want - 1) / want;
+    s.n_split = (nt + s.tiles_per_split - 1) / s.tiles_per_split;
+  }
   s.ys_stride = hm::align_up((size_t)a->Di, 64);
   s.part_b_stride = hm::align_up((size_t)a->Hkv * s.n_split * s.grp * (a->Dh + 2), 64);
   s.ys_bytes = (size_t)a->B * s.ys_stride * sizeof(float);
@@ -553,7 +667,7 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
     HM_PTR(a->v_new);
   }
   HM_REQUIRE((double)a->B * (a->n_meta + a->cache_slots) * a->Hkv * a->Dh < 4.0e9 &&
-                 (double)a->B * a->Hkv * (a->n_meta + a->cache_slots) / kKeysPerWG < 1.0e9,
+                 (double)a->B * a->Hkv * (a->n_meta + a->cache_slots) / 64 < 1.0e9,
              HM_ERR_UNSUPPORTED, "cache too large");
   const StepGeom g = step_geom(a);
   const size_t need = g.ys_bytes + g.part_bytes;
@@ -573,15 +687,16 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
 
   if (a->dtype == HM_BF16) {
     const int n_attn = a->B * a->Hkv * g.n_split;
-    const int ssm_per_b = (a->Di + 255) / 256;
-    hipLaunchKernelGGL(step_fused_bf16, dim3(n_attn + a->B * ssm_per_b), dim3(256), 0, st,
+    const int n_ssm = a->B * a->Di;
+    const int ssm_per_block = (n_ssm + n_attn - 1) / n_attn;
+    hipLaunchKernelGGL(step_fused_bf16, dim3(n_attn), dim3(256), 0, st,
                        (const bf16_t*)a->q, (const bf16_t*)a->k_new, (const bf16_t*)a->v_new,
                        (bf16_t*)a->k_cache, (bf16_t*)a->v_cache, (const bf16_t*)a->x,
                        (const bf16_t*)a->delta, (const bf16_t*)a->Bm, (const bf16_t*)a->Cm,
                        (const bf16_t*)a->z, a->A, a->D, a->conv_w, a->conv_b, a->conv_state,
                        a->ssm_state, ys_ws, g.ys_stride, part, g.part_b_stride, a->Hq, a->Hkv,
                        a->Di, S, g.L, slot, pos, sc, l2b, exp2(-l2b / 32.0), g.n_split,
-                       n_attn, ssm_per_b);
+                       g.tiles_per_split, ssm_per_block, n_ssm);
     hm_status s = hm::check_launch("step_fused_bf16");
     if (s != HM_OK) return s;
     hipLaunchKernelGGL(step_combine<bf16_t>, dim3(a->B), dim3(kCombThreads), 0, st,

@@ -55,7 +55,10 @@ def test_workspace_queries():
     a = hm.StepArgs(B=64, Hq=25, Hkv=5, Dh=64, Di=1600, N=16, K=4, n_meta=128, window=1024,
                     cache_slots=1024, n_prev=2048, dtype=hm.HM_BF16)
     nb = L.hm_mixer_step_workspace(ctypes.byref(a))
-    assert nb >= 64 * 1600 * 4 + 64 * 5 * 5 * 5 * 66 * 4
+    # SSM branch output + at least one (max, sum, O) partial per (sequence, head)
+    assert nb >= 64 * 1600 * 4 + 64 * 25 * 66 * 4
+    a.dtype = hm.HM_F32
+    assert L.hm_mixer_step_workspace(ctypes.byref(a)) >= 64 * 1600 * 4 + 64 * 25 * 66 * 4
 
 
 FAKE = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced: every call below fails validation
