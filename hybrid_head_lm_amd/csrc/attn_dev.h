@@ -253,6 +253,7 @@ HM_DEV void attn_fwd_bf16_body(
     // S^T - m_ref (accumulated onto -m_ref); the two 32-key blocks are
     // independent accumulation chains, alternated
     const unsigned char* sk = smem[it % kStages][0];
+    __builtin_amdgcn_s_setprio(1);
     f32x16_v S[2];
     S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_v*)(sk + lds_off(n, gq)),
                                                    qf[0], cinit, 0, 0, 0);
@@ -264,6 +265,7 @@ HM_DEV void attn_fwd_bf16_body(
       for (int kb = 0; kb < 2; ++kb)
         S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             *(const bf16x8_v*)(sk + lds_off(kb * 32 + n, 2 * k4 + gq)), qf[k4], S[kb], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
     if (cls == 1 || j0 + kBN > T) {
       // element (kb, i) is key kbase + off with off = 32 kb + 16 (i / 8) + i % 8;
       // visible iff off <= a and (off < mm or off >= w)  (hm_visible, shifted)
@@ -285,7 +287,11 @@ HM_DEV void attn_fwd_bf16_body(
     for (int i = 2; i < 16; ++i) mx = fmaxf(mx, S[0][i]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[1][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(mx), __float_as_int(mx),
+                                                       false, false);
+      mx = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+    }
     const bool need = fresh ? (mx > NEG_INF) : (mx > 8.f);
     if (__ballot(need) != 0) {
       // move the reference: rescale O and l and shift this tile's scores

@@ -224,9 +224,11 @@ HM_DEV void scan_chunk_body(
           Cv[4 * i] = t4.x; Cv[4 * i + 1] = t4.y; Cv[4 * i + 2] = t4.z; Cv[4 * i + 3] = t4.w;
         }
         float ys4[4] = {Dc * xv, 0.f, 0.f, 0.f};
+        // decay product first, then the input term accumulated onto it: both
+        // steps update h in place (no register copies in the loop)
 #pragma unroll
         for (int nn = 0; nn < kNS; ++nn) {
-          h[nn] = fast_exp2(dv * a2[nn]) * h[nn] + du * Bv[nn];
+          h[nn] = fmaf(du, Bv[nn], fast_exp2(dv * a2[nn]) * h[nn]);
           ys4[nn & 3] += Cv[nn] * h[nn];
         }
         float yv = (ys4[0] + ys4[1]) + (ys4[2] + ys4[3]);
@@ -238,7 +240,7 @@ HM_DEV void scan_chunk_body(
         }
       } else {
 #pragma unroll
-        for (int nn = 0; nn < kNS; ++nn) h[nn] = fast_exp2(dv * a2[nn]) * h[nn] + du * Bv[nn];
+        for (int nn = 0; nn < kNS; ++nn) h[nn] = fmaf(du, Bv[nn], fast_exp2(dv * a2[nn]) * h[nn]);
         ssum += dv;
       }
     }
