@@ -42,8 +42,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ Kr, const bf16_t* __restrict__ Vt,
     bf16_t* __restrict__ o, int T, int Tpad, int Hq, int Hkv, int M, int W, long long pos0,
     float qscale, double rstep, int n_qt, int n_groups) {
-  attn_fwd_bf16_body(blockIdx.x, q, Kr, Vt, o, T, Tpad, Hq, Hkv, M, W, pos0, qscale, rstep, n_qt,
-                     n_groups);
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][8192];
+  attn_fwd_bf16_body(smem, blockIdx.x, q, Kr, Vt, o, T, Tpad, Hq, Hkv, M, W, pos0, qscale, rstep,
+                     n_qt, n_groups);
 }
 
 // ---------------------------------------------------------------- float32 path

@@ -122,12 +122,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // A workgroup of 4 waves owns 128 query rows of one head (32 per wave) and
 // walks the key tiles visible from them: the meta tiles, then the window.
+// smem: the workgroup's kStages x 2 x 8 KB of LDS (K and V^T tile per stage).
 HM_DEV void attn_fwd_bf16_body(
-    int bid, const bf16_t* __restrict__ q, const bf16_t* __restrict__ Kr,
+    unsigned char (*smem)[2][8192], int bid, const bf16_t* __restrict__ q, const bf16_t* __restrict__ Kr,
     const bf16_t* __restrict__ Vt, bf16_t* __restrict__ o, int T, int Tpad, int Hq, int Hkv,
     int M, int W, long long pos0, float qscale, double rstep, int n_qt, int n_groups) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][8192];
-
   // Work item.  A group is (query tile, b, kv head) and its items are the
   // Hq/Hkv query heads that read the same K/V.  Groups are ranked heaviest
   // first (the visible key count never decreases with the query tile), rank r

@@ -8,9 +8,13 @@
 // work items that do not depend on each other share one launch, taking
 // disjoint ranges of the grid:
 //   1. K/V pre-pass (rotate K, lay out V)   | chunk aggregates of the scan
-//   2. flash attention                      | carry across scan chunks
-//   3. final scan pass (y and the final states)
-//   4. branch norm and average
+//   2. flash attention                      | final scan pass: each chunk wave
+//                                             composes its own incoming state
+//                                             from the aggregates, then runs
+//                                             the chunk (y, final states)
+//   3. branch norm and average
+// The attention is latency bound at well under one workgroup per SIMD and the
+// scan is VALU bound, so the two fill each other's idle issue slots in launch 2.
 // The same device code as the standalone entry points runs in each range.
 #include "attn_dev.h"
 #include "ssm_dev.h"
@@ -44,39 +48,96 @@ __global__ __launch_bounds__(64) void prefill_prep_agg(
   bid -= pg.n;
   const int gxi = bid % ag.gx, kc = (bid / ag.gx) % ag.nA, b = bid / (ag.gx * ag.nA);
   // (the aggregate pass reads neither C, D, z nor writes y: B stands in for C)
-  scan_chunk_body<bf16_t, true, false, true>(gxi, kc, b, x, dl, A, Bm, Bm, nullptr, nullptr, cw,
-                                              cb, nullptr, nullptr, E, S, nullptr, nullptr, T, Di,
-                                              L, nC);
+  __shared__ ScanLds<bf16_t, false> sm;
+  scan_chunk_body<bf16_t, true, false, true>(&sm, nullptr, gxi, kc, b, x, dl, A, Bm, Bm, nullptr,
+                                              nullptr, cw, cb, nullptr, nullptr, E, S, nullptr,
+                                              nullptr, T, Di, L, nC);
 }
 
-constexpr int kFusedRanges = 4;   // carry waves per 256-thread workgroup
+constexpr int kChunkWaves = 4;        // consecutive chunks per 256-thread workgroup
+constexpr int kAttnLds = kStages * 2 * 8192;
+constexpr int kOwnCarryBatch = 16;    // chunk maps loaded at once per wave
+static_assert(sizeof(ScanLds<bf16_t, true>) <= 8192, "a chunk wave's LDS is 8 KB");
+static_assert(kChunkWaves * 8192 <= kAttnLds, "chunk waves reuse the attention ring");
+static_assert(kChunkWaves * kNS * 64 * 4 <= kAttnLds, "incoming states fit the ring");
+
+struct FinalGeom {
+  int gx, nJ;   // 64-channel groups; workgroups per group and batch (kChunkWaves chunks each)
+};
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void
-prefill_attn_carry(int n_attn, const bf16_t* __restrict__ q, const bf16_t* __restrict__ Kr,
-                   const bf16_t* __restrict__ Vt, bf16_t* __restrict__ o, int T, int Tpad, int Hq,
+prefill_attn_final(int n_attn, const bf16_t* __restrict__ q, const bf16_t* __restrict__ Kr,
+                   const bf16_t* __restrict__ Vt, bf16_t* __restrict__ o, int Tpad, int Hq,
                    int Hkv, int M, int W, long long pos0, float qscale, double rstep, int n_qt,
-                   int n_groups, int gx, const float* __restrict__ A, float* __restrict__ E,
-                   const float* __restrict__ S, int Di, int nC) {
+                   int n_groups, FinalGeom fg, const bf16_t* __restrict__ x,
+                   const bf16_t* __restrict__ dl, const float* __restrict__ A,
+                   const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
+                   const float* __restrict__ D, const bf16_t* __restrict__ z,
+                   const float* __restrict__ cw, const float* __restrict__ cb,
+                   float* __restrict__ cst_out, float* __restrict__ E, float* __restrict__ S,
+                   bf16_t* __restrict__ y, float* __restrict__ h_out, int T, int Di, int L,
+                   int nC) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kAttnLds];
   int bid = blockIdx.x;
   if (bid < n_attn) {
-    attn_fwd_bf16_body(bid, q, Kr, Vt, o, T, Tpad, Hq, Hkv, M, W, pos0, qscale, rstep, n_qt,
-                       n_groups);
+    attn_fwd_bf16_body((unsigned char(*)[2][8192])smem, bid, q, Kr, Vt, o, T, Tpad, Hq, Hkv, M,
+                       W, pos0, qscale, rstep, n_qt, n_groups);
     return;
   }
   bid -= n_attn;
-  const int gxi = bid % gx, nn = (bid / gx) % kNS, b = bid / (gx * kNS);
-  scan_carry_body<kFusedRanges>(gxi, nn, b, A, nullptr, E, S, Di, nC);
-}
+  const int gxi = bid % fg.gx, jw = (bid / fg.gx) % fg.nJ, b = bid / (fg.gx * fg.nJ);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int k0 = jw * kChunkWaves, k = k0 + wave;
+  const int c = min(gxi * 64 + lane, Di - 1);
+  // states entering chunks k0 .. k0+3: [chunk - k0][state][lane]
+  float(*sH)[kNS][64] = (float(*)[kNS][64])smem;
 
-__global__ __launch_bounds__(64) void prefill_scan_final(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ dl, const float* __restrict__ A,
-    const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm, const float* __restrict__ D,
-    const bf16_t* __restrict__ z, const float* __restrict__ cw, const float* __restrict__ cb,
-    float* __restrict__ cst_out, float* __restrict__ E, float* __restrict__ S,
-    bf16_t* __restrict__ y, float* __restrict__ h_out, int T, int Di, int L, int nC) {
-  scan_chunk_body<bf16_t, true, true, true>(blockIdx.x, blockIdx.y, blockIdx.z, x, dl, A, Bm, Cm,
-                                             D, z, cw, cb, nullptr, cst_out, E, S, y, h_out, T,
-                                             Di, L, nC);
+  // 1. Chunk kk < nC-1 maps the state h to exp2(a2 * S_kk) h + E_kk (sum of
+  //    delta, end state from a zero start).  Composing the maps of chunks
+  //    0 .. kk-1 from h = 0 gives the state entering chunk kk.  Wave w
+  //    composes states 4w .. 4w+3 of the 64 channels up to the workgroup's
+  //    last chunk and keeps the states entering each of its chunks.
+  {
+    float a2[4], H[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a2[e] = A[c * kNS + 4 * wave + e] * kLog2e;
+    const int kend = min(k0 + kChunkWaves, nC) - 1;   // compose chunks 0 .. kend-1
+    const float* ep = E + ((size_t)b * nC * kNS + 4 * wave) * Di + c;
+    const float* sp = S + (size_t)b * nC * Di + c;
+    auto stash = [&](int j) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sH[j][4 * wave + e][lane] = H[e];
+    };
+    if (k0 == 0) stash(0);
+    for (int kb = 0; kb < kend; kb += kOwnCarryBatch) {
+      float gs[kOwnCarryBatch], ge[kOwnCarryBatch][4];
+#pragma unroll
+      for (int i = 0; i < kOwnCarryBatch; ++i) {
+        const int kk = min(kb + i, kend - 1);   // clamped, unconditional loads
+        gs[i] = sp[(size_t)kk * Di];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ge[i][e] = ep[((size_t)kk * kNS + e) * Di];
+      }
+#pragma unroll
+      for (int i = 0; i < kOwnCarryBatch; ++i)
+        if (kb + i < kend) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) H[e] = fast_exp2(a2[e] * gs[i]) * H[e] + ge[i][e];
+          if (kb + i + 1 >= k0) stash(kb + i + 1 - k0);
+        }
+    }
+  }
+  __syncthreads();
+  float h[kNS];
+#pragma unroll
+  for (int nn = 0; nn < kNS; ++nn) h[nn] = sH[wave][nn][lane];
+  __syncthreads();   // the states lie where the chunk waves stage their data
+  if (k >= nC) return;
+  // 3. The chunk itself, in this wave's 8 KB of the (idle) attention ring.
+  scan_chunk_body<bf16_t, true, true, true, true>(
+      (ScanLds<bf16_t, true>*)(smem + wave * 8192), h, gxi, k, b, x, dl, A, Bm, Cm, D, z, cw, cb,
+      nullptr, cst_out, E, S, y, h_out, T, Di, L, nC);
 }
 
 }  // namespace
@@ -105,7 +166,7 @@ hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, 
   float* S = E + (size_t)B * nC * kNS * Di;
   const int gx = (Di + 63) / 64;
 
-  // 1. K/V pre-pass | chunk aggregates
+  // 1. K/V pre-pass | chunk aggregates (chunks 0 .. nC-2)
   PrepGeom pg{a->kv_reuse ? 0 : (Tpad / 16) * Hkv * B, Tpad / 16, Hkv};
   AggGeom ag{gx * (nC - 1) * B, gx, nC > 1 ? nC - 1 : 1};
   if (pg.n + ag.n > 0) {
@@ -116,25 +177,22 @@ hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, 
     hm_status s = check_launch("prefill_prep_agg");
     if (s != HM_OK) return s;
   }
-  // 2. attention | carry
+  // 2. attention | final scan pass
   const int n_qt = (T + 128 - 1) / 128;
   const int n_groups = B * Hkv * n_qt;
   const int n_attn = 8 * ((n_groups + 7) / 8) * (Hq / Hkv);
-  const int n_carry = gx * kNS * B;
-  hipLaunchKernelGGL(prefill_attn_carry, dim3(n_attn + n_carry), dim3(256), 0, st, n_attn,
-                     (const bf16_t*)a->q, (const bf16_t*)Kr, (const bf16_t*)Vt, (bf16_t*)a->ya, T,
+  const FinalGeom fg{gx, (nC + kChunkWaves - 1) / kChunkWaves};
+  const int n_final = fg.gx * fg.nJ * B;
+  hipLaunchKernelGGL(prefill_attn_final, dim3(n_attn + n_final), dim3(256), 0, st, n_attn,
+                     (const bf16_t*)a->q, (const bf16_t*)Kr, (const bf16_t*)Vt, (bf16_t*)a->ya,
                      Tpad, Hq, Hkv, a->n_meta, a->window, a->pos0, scale * kLog2e, rstep, n_qt,
-                     n_groups, gx, a->A, E, (const float*)S, Di, nC);
-  hm_status s = check_launch("prefill_attn_carry");
+                     n_groups, fg, (const bf16_t*)a->x, (const bf16_t*)a->delta, a->A,
+                     (const bf16_t*)a->Bm, (const bf16_t*)a->Cm, a->D, (const bf16_t*)a->z,
+                     a->conv_w, a->conv_b, a->conv_state_out, E, S, (bf16_t*)a->ys, a->h_out, T,
+                     Di, L, nC);
+  hm_status s = check_launch("prefill_attn_final");
   if (s != HM_OK) return s;
-  // 3. final scan pass
-  hipLaunchKernelGGL(prefill_scan_final, dim3(gx, nC, B), dim3(64), 0, st, (const bf16_t*)a->x,
-                     (const bf16_t*)a->delta, a->A, (const bf16_t*)a->Bm, (const bf16_t*)a->Cm,
-                     a->D, (const bf16_t*)a->z, a->conv_w, a->conv_b, a->conv_state_out, E, S,
-                     (bf16_t*)a->ys, a->h_out, T, Di, L, nC);
-  s = check_launch("prefill_scan_final");
-  if (s != HM_OK) return s;
-  // 4. branch norm and average
+  // 3. branch norm and average
   return norm_mean_impl(a->ya, a->ys, a->beta_a, a->beta_s, a->eps, a->out, (long long)B * T, Di,
                         a->dtype, st, /*dry=*/false);
 }

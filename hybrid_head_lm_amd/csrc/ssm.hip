@@ -72,9 +72,10 @@ __global__ __launch_bounds__(64) void scan_chunk(
     const float* __restrict__ cst_in, float* __restrict__ cst_out, float* __restrict__ E,
     float* __restrict__ S, Tact* __restrict__ y, float* __restrict__ h_out, int T, int Di, int L,
     int nC) {
-  scan_chunk_body<Tact, CONV, FINAL, VEC>(blockIdx.x, blockIdx.y, blockIdx.z, x, dl, A, Bm, Cm,
-                                          D, z, cw, cb, cst_in, cst_out, E, S, y, h_out, T, Di,
-                                          L, nC);
+  __shared__ ScanLds<Tact, FINAL> sm;
+  scan_chunk_body<Tact, CONV, FINAL, VEC>(&sm, nullptr, blockIdx.x, blockIdx.y, blockIdx.z, x, dl,
+                                          A, Bm, Cm, D, z, cw, cb, cst_in, cst_out, E, S, y, h_out,
+                                          T, Di, L, nC);
 }
 
 constexpr int kRanges = 8;

@@ -88,8 +88,40 @@ template <typename Tact> struct SubRows;
 template <> struct SubRows<bf16_t> { static constexpr int value = 16; };
 template <> struct SubRows<float> { static constexpr int value = 8; };
 
-template <typename Tact, bool CONV, bool FINAL, bool VEC>
+// LDS of one chunk wave: the staged sub-block.  The y of a step is written
+// over the x of that step (each lane its own element, already consumed).
+template <typename Tact, bool FINAL>
+struct ScanLds {
+  static constexpr int R = SubRows<Tact>::value;
+  __attribute__((aligned(16))) Tact sx[R][64];
+  __attribute__((aligned(16))) Tact sd[R][64];
+  __attribute__((aligned(16))) Tact sz[FINAL ? R : 1][64];
+  __attribute__((aligned(16))) float sB[R][kNS];
+  __attribute__((aligned(16))) float sC[FINAL ? R : 1][kNS];
+};
+
+// Orders a wave's LDS writes before its later LDS reads.  The sub-block
+// staging is wave-local (every lane reads what lanes of its own wave wrote, and
+// LDS executes a wave's operations in order), so a workgroup that runs
+// independent chunk waves needs no workgroup barrier; a one-wave workgroup
+// uses the plain barrier.
+template <bool WAVE_LOCAL>
+HM_DEV void chunk_sync() {
+  if constexpr (WAVE_LOCAL) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
+}
+
+// sm: this wave's LDS.  h_init (FINAL only): the state entering the chunk, in
+// the caller's registers, or nullptr to read it from E (written there by the
+// carry pass).
+template <typename Tact, bool CONV, bool FINAL, bool VEC, bool WAVE_LOCAL = false>
 HM_DEV void scan_chunk_body(
+    ScanLds<Tact, FINAL>* sm, const float* h_init,
     int gxi, int k, int b, const Tact* __restrict__ x, const Tact* __restrict__ dl, const float* __restrict__ A,
     const Tact* __restrict__ Bm, const Tact* __restrict__ Cm, const float* __restrict__ D,
     const Tact* __restrict__ z, const float* __restrict__ cw, const float* __restrict__ cb,
@@ -101,13 +133,13 @@ HM_DEV void scan_chunk_body(
   constexpr int CPR = 64 / PC;                   // chunks per 64-channel row
   static_assert(R * CPR == 128, "two 16-byte chunks per lane per tensor");
   static_assert(R * kNS / PC <= 64, "one B (or C) chunk per lane");
-  __shared__ __attribute__((aligned(16))) Tact sx[R][64];
-  __shared__ __attribute__((aligned(16))) Tact sd[R][64];
-  __shared__ __attribute__((aligned(16))) Tact sz[FINAL ? R : 1][64];
-  __shared__ __attribute__((aligned(16))) float sB[R][kNS];
-  __shared__ __attribute__((aligned(16))) float sC[FINAL ? R : 1][kNS];
-  __shared__ __attribute__((aligned(16))) Tact sy[FINAL && VEC ? R : 1][64];
-  const int lane = threadIdx.x;
+  auto& sx = sm->sx;
+  auto& sd = sm->sd;
+  auto& sz = sm->sz;
+  auto& sB = sm->sB;
+  auto& sC = sm->sC;
+  auto& sy = sm->sx;
+  const int lane = threadIdx.x & 63;
   const int c0 = gxi * 64;
   const bool active = c0 + lane < Di;
   const int c = active ? c0 + lane : Di - 1;
@@ -171,7 +203,7 @@ HM_DEV void scan_chunk_body(
 #pragma unroll
   for (int nn = 0; nn < kNS; ++nn) {
     a2[nn] = A[c * kNS + nn] * kLog2e;
-    h[nn] = FINAL ? hin[(size_t)nn * Di] : 0.f;
+    h[nn] = FINAL ? (h_init ? h_init[nn] : hin[(size_t)nn * Di]) : 0.f;
   }
   const float Dc = (FINAL && D) ? D[c] : 0.f;
   const Tact* xc = xb + c;
@@ -244,7 +276,7 @@ HM_DEV void scan_chunk_body(
         ssum += dv;
       }
     }
-    __syncthreads();
+    chunk_sync<WAVE_LOCAL>();
     if constexpr (FINAL && VEC) {
       // y sub-block out as two 16-byte stores per lane.  Rows past nt and
       // chunks past Di are clamped onto a valid row / chunk, so such a lane
@@ -262,12 +294,12 @@ HM_DEV void scan_chunk_body(
   for (; ts + R < t1; ts += R) {
     if constexpr (VEC) {
       store();
-      __syncthreads();
+      chunk_sync<WAVE_LOCAL>();
       load(ts + R, min(R, t1 - ts - R));
     } else {
       stage_scalar<Tact, R>(sx, sd, sz, sB, sC, xb, db, zb, Bb, Cb, has_z, FINAL, ts, R, c0, Di,
                             lane);
-      __syncthreads();
+      chunk_sync<WAVE_LOCAL>();
     }
     run(ts, R);
   }
@@ -277,7 +309,7 @@ HM_DEV void scan_chunk_body(
     stage_scalar<Tact, R>(sx, sd, sz, sB, sC, xb, db, zb, Bb, Cb, has_z, FINAL, ts, t1 - ts, c0,
                           Di, lane);
   }
-  __syncthreads();
+  chunk_sync<WAVE_LOCAL>();
   run(ts, t1 - ts);
 
   if (!FINAL) {

@@ -171,7 +171,7 @@ hm_status hm_branch_norm_mean(const void* ya, const void* ys, const float* beta_
  * stream2 (optional, a hipStream_t as void*): when set, the SSM branch runs on
  * it, concurrently with attention on `stream` (the two head types are
  * independent until the fusion); `stream` waits for it before the fusion.
- * Without stream2 a bf16 layer runs as four launches on `stream` in which
+ * Without stream2 a bf16 layer runs as three launches on `stream` in which
  * independent parts share a launch.
  * Workspace: hm_mixer_prefill_workspace() bytes, queried with the same
  * shapes, dtype and kv as the call.  Layers that run one after the other on

@@ -206,7 +206,7 @@ def test_mixer_prefill(shape):
 
 
 # bf16 layers on one stream take the fused launch sequence (pre-pass | chunk
-# aggregates, attention | carry, final pass, norm): short sequences with a
+# aggregates, attention | final pass with its own carry, norm): short sequences with a
 # single scan chunk, ragged lengths, several sequences, global attention
 @pytest.mark.parametrize("B,M,N,W,Hq,Hkv", [(1, 4, 20, 16, 5, 5), (1, 5, 77, 32, 4, 2),
                                             (2, 16, 300, 64, 10, 5), (3, 0, 129, 0, 5, 1),
