@@ -78,13 +78,16 @@ prefill_attn_final(int n_attn, const bf16_t* __restrict__ q, const bf16_t* __res
                    bf16_t* __restrict__ y, float* __restrict__ h_out, int T, int Di, int L,
                    int nC) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kAttnLds];
+  // The final-pass workgroups take the low ids (dispatched first), the latest
+  // chunks (longest own carry) first; the attention workgroups follow.
+  const int n_fin = (int)gridDim.x - n_attn;
   int bid = blockIdx.x;
-  if (bid < n_attn) {
-    attn_fwd_bf16_body((unsigned char(*)[2][8192])smem, bid, q, Kr, Vt, o, T, Tpad, Hq, Hkv, M,
-                       W, pos0, qscale, rstep, n_qt, n_groups);
+  if (bid >= n_fin) {
+    attn_fwd_bf16_body((unsigned char(*)[2][8192])smem, bid - n_fin, q, Kr, Vt, o, T, Tpad, Hq,
+                       Hkv, M, W, pos0, qscale, rstep, n_qt, n_groups);
     return;
   }
-  bid -= n_attn;
+  bid = n_fin - 1 - bid;
   const int gxi = bid % fg.gx, jw = (bid / fg.gx) % fg.nJ, b = bid / (fg.gx * fg.nJ);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
