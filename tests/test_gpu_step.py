@@ -113,3 +113,34 @@ def test_decode_repeated_calls_reuse_workspace():
         lb["conv_state"], lb["ssm_state"] = rb["conv_state"], rb["ssm_state"]
         kc, vc = ra["k_cache"], ra["v_cache"]
     assert_close(down(t["a"]["ssm_state"]), la["ssm_state"], "bf16", "state after 3 calls")
+
+
+def test_decode_pair_shared_garbage_workspace():
+    """Producer and consumer share one workspace that starts out as random
+    bytes (no part of it may need clearing); the batch of 3 makes the SSM
+    shares of workgroups straddle sequences.  Two calls in a row."""
+    shape = with_(DECODE_PAIR, B=3, n_prev=333)
+    d = decode_inputs(shape, 8)
+    t = up_inputs(d, shape.dtype)
+    gen = torch.Generator(device="cpu").manual_seed(4)
+    probe = hm.StepPlan(t["a"], t["k_cache"], t["v_cache"], shape.n_prev, shape.M, shape.W)
+    nb = probe.ws.numel()
+    ws = torch.randint(0, 256, (nb,), dtype=torch.uint8, generator=gen).to("cuda")
+    pa = hm.StepPlan(t["a"], t["k_cache"], t["v_cache"], shape.n_prev, shape.M, shape.W,
+                     workspace=ws)
+    pb = hm.StepPlan(t["b"], t["k_cache"], t["v_cache"], shape.n_prev, shape.M, shape.W,
+                     workspace=ws)
+    la, lb = dict(d["a"]), dict(d["b"])
+    kc, vc = d["k_cache"], d["v_cache"]
+    for it in range(2):
+        pa.run()
+        pb.run()
+        torch.cuda.synchronize()
+        ra = oracle.mixer_step(la, kc, vc, shape.n_prev, shape.M, shape.W, producer=True)
+        rb = oracle.mixer_step(lb, ra["k_cache"], ra["v_cache"], shape.n_prev, shape.M, shape.W,
+                               producer=False)
+        assert_close(down(pa.out), ra["out"], "bf16", f"producer out, call {it}")
+        assert_close(down(pb.out), rb["out"], "bf16", f"consumer out, call {it}")
+        la["conv_state"], la["ssm_state"] = ra["conv_state"], ra["ssm_state"]
+        lb["conv_state"], lb["ssm_state"] = rb["conv_state"], rb["ssm_state"]
+        kc, vc = ra["k_cache"], ra["v_cache"]
