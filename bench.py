@@ -20,7 +20,16 @@ Also reported on the same JSON line:
                 the global-attention layer (batch 4, 128 + 8192 tokens) and the
                 32-layer stack (batch 2, 128 + 16384 tokens, layers 0/15/31
                 global, adjacent sliding-window layers sharing prepared K/V);
+  layer_step_us single-call times of the step (median, p10, p90) after the timed
+                region, and the shader clock the driver reports;
+  ssm_branch    the conv + scan branch on its own against HBM and against the
+                non-packed fp32 VALU rate (single-pass VALU work per
+                token-channel);
   cpu_baseline  the float64 CPU oracle on one whole layer of the step's workload.
+HBM traffic (`traffic`) of the attention kernel, the SSM branch and the decode
+pair comes from the committed rocprofv3 counter summaries in profiles/ (null
+once the kernel sources differ from those the counters were taken with);
+`--counters` is the run those summaries are taken over.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
                        [--no-cpu-baseline] [--counters]
@@ -40,9 +49,19 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 COPY_BYTES = 256 << 20      # calibration copy for the HBM byte counters
-# sources of the attention kernel whose counters profiles/ holds
+# sources of the kernels whose HBM counters profiles/ holds
 ATTN_SOURCES = ("hybrid_head_lm_amd/csrc/attn_dev.h", "hybrid_head_lm_amd/csrc/attn.hip",
                 "hybrid_head_lm_amd/csrc/hm_common.h")
+SSM_SOURCES = ("hybrid_head_lm_amd/csrc/ssm_dev.h", "hybrid_head_lm_amd/csrc/ssm.hip",
+               "hybrid_head_lm_amd/csrc/hm_common.h")
+STEP_SOURCES = ("hybrid_head_lm_amd/csrc/step.hip", "hybrid_head_lm_amd/csrc/hm_common.h")
+PEAK_VALU_LANE_OPS = 256 * 64 * 2.4e9   # non-packed fp32 VALU: 64 lanes/clk/CU
+# single-pass VALU work of the SSM branch per token-channel: per state the decay
+# product, exp, h product, input term, output term (4 VALU + 1 transcendental);
+# per token-channel the conv (4), SiLU of the conv (3 + 2), delta*x (1), D*x (1),
+# the gate SiLU(z) (3 + 2) and the gate product (1)
+SCAN_VALU_PER_TC = 16 * 4 + 4 + 3 + 1 + 1 + 3 + 1
+SCAN_TRANS_PER_TC = 16 + 2 + 2
 
 
 def attn_flops(shape) -> float:
@@ -85,9 +104,10 @@ def _sources_hash(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel_srcs, summary: str):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
-    when there is none or the kernel sources changed since it was taken."""
+def traffic_from_profile(kernel_srcs, summary: str, key: str = "hbm_bytes_per_launch"):
+    """HBM bytes (per launch, or per the unit `key` names) from a committed
+    rocprofv3 counter summary, or None when there is none or the kernel sources
+    changed since it was taken."""
     path = os.path.join(ROOT, "profiles", summary)
     if not os.path.exists(path):
         return None
@@ -99,7 +119,7 @@ def traffic_from_profile(kernel_srcs, summary: str):
     if vals.get("source_sha256_16") != _sources_hash(kernel_srcs):
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
 
@@ -119,6 +139,50 @@ def timed(fn, steps: int, warmup: int, stream=None):
     e1.record(s)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def step_percentiles(fn, steps: int, while_busy=None):
+    """Median, p10 and p90 of single-call times (microseconds), one HIP event
+    pair around each call, after the timed region (a distribution, not the
+    headline figure).  `while_busy` runs on the host once every call is queued,
+    while the GPU is still working through them."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    if while_busy is not None:
+        while_busy()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    pick = lambda q: us[min(len(us) - 1, int(q * (len(us) - 1) + 0.5))]
+    return {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9), "calls": len(us)}
+
+
+def gpu_sclk_mhz():
+    """Current shader clock from the driver's sysfs table (the line marked *),
+    or None where it cannot be read."""
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(f):
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(shape, inp, min_seconds: float = 10.0):
@@ -141,7 +205,7 @@ def cpu_baseline(shape, inp, min_seconds: float = 10.0):
         if dt >= min_seconds:
             break
     return {"value": n * shape.B * shape.T / dt, "unit": "tokens/s", "cores": threads or 1,
-            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{n} whole prefill layers of {shape.name} (float64 NumPy, same "
                       f"inputs each time), {dt:.1f} s"}
 
@@ -212,12 +276,29 @@ def main():
         for _ in range(3):
             hm.attn_with_kv(t["q"], plan.kv, shape.Hkv, shape.M, shape.W, shape.rope_base,
                             out=plan.ya)
+        for _ in range(3):
+            hm.conv_selective_scan(t["x"], t["conv_w"], t["conv_b"], t["delta"], t["A"],
+                                   t["Bm"], t["Cm"], t["D"], t["z"], out=plan.ys)
+        for _ in range(3):
+            plan.run()
+        dshape = DECODE_PAIR
+        d = to_device(decode_inputs(dshape, 0), dshape.dtype)
+        pa = hm.StepPlan(d["a"], d["k_cache"], d["v_cache"], dshape.n_prev, dshape.M, dshape.W)
+        pb = hm.StepPlan(d["b"], d["k_cache"], d["v_cache"], dshape.n_prev, dshape.M, dshape.W)
+        for _ in range(3):
+            pa.run()
+            pb.run()
         torch.cuda.synchronize()
-        print("counters run done: 3 copies of", COPY_BYTES, "bytes, 3 attention launches")
+        print("counters run done: 3 copies of", COPY_BYTES, "bytes, then 3 each of the "
+              "attention launch, the SSM branch, the fused layer and the decode pair")
         return
 
     # the step: one mixer layer (both branches on one stream, kernels in order)
     plan, ms = run_prefill(shape, hm, t, args.steps, args.warmup, two_streams=False)
+    sclk = []
+    layer_dist = step_percentiles(plan.run, max(20, args.steps),
+                                  while_busy=lambda: sclk.append(gpu_sclk_mhz()))
+    sclk = sclk[0] if sclk else None
     _, ms_two = run_prefill(shape, hm, t, args.steps, args.warmup, two_streams=True)
     tokens = shape.B * shape.T
 
@@ -230,6 +311,7 @@ def main():
     traffic = traffic_from_profile(ATTN_SOURCES, "attn_fwd_bf16.swa-prefill-b1-t2176.pmc.txt")
 
     # SSM branch and fusion on their own (context for the breakdown)
+    tc_ssm = shape.B * shape.T * shape.Di
     ms_ssm = timed(lambda: hm.conv_selective_scan(t["x"], t["conv_w"], t["conv_b"], t["delta"],
                                                   t["A"], t["Bm"], t["Cm"], t["D"], t["z"],
                                                   out=plan.ys), args.steps, args.warmup)
@@ -293,12 +375,25 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "algorithmic_flop_per_launch": fl, "ms_per_launch": ms_attn},
+        "layer_step_us": layer_dist,
+        "sclk_mhz": sclk,     # read from the driver while the layer calls run
         "breakdown_ms": {"layer_one_stream": ms, "layer_two_streams": ms_two,
                          "attention_kernel": ms_attn, "ssm_branch": ms_ssm,
                          "norm_mean": ms_norm},
         "ssm_branch": {"bound": "hbm", "achieved": scan_bytes(shape) / (ms_ssm * 1e-3) / 1e9,
                        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                       "frac": scan_bytes(shape) / (ms_ssm * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+                       "frac": scan_bytes(shape) / (ms_ssm * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                       "traffic": traffic_from_profile(
+                           SSM_SOURCES, "ssm-branch.swa-prefill-b1-t2176.pmc.txt",
+                           "hbm_bytes_per_call"),
+                       "alu": {"bound": "alu", "unit": "lane-op/s",
+                               "valu_per_token_channel": SCAN_VALU_PER_TC,
+                               "transcendental_per_token_channel": SCAN_TRANS_PER_TC,
+                               "achieved": tc_ssm * (SCAN_VALU_PER_TC + SCAN_TRANS_PER_TC)
+                                           / (ms_ssm * 1e-3),
+                               "peak": PEAK_VALU_LANE_OPS,
+                               "frac": tc_ssm * (SCAN_VALU_PER_TC + SCAN_TRANS_PER_TC)
+                                       / (ms_ssm * 1e-3) / PEAK_VALU_LANE_OPS}},
         "decode": {"workload": dshape.name, "steps_per_s": 1e3 / ms_dec_cold,
                    "tokens_per_s": dshape.B * 1e3 / ms_dec_cold, "ms_per_step": ms_dec_cold,
                    "cache": "cold (Infinity Cache flushed before every step: 512 MB "
@@ -307,7 +402,10 @@ def main():
                                 "achieved": dbytes / (ms_dec_cold * 1e-3) / 1e9,
                                 "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                                 "frac": dbytes / (ms_dec_cold * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                                "algorithmic_bytes_per_step": dbytes},
+                                "algorithmic_bytes_per_step": dbytes,
+                                "traffic": traffic_from_profile(
+                                    STEP_SOURCES, "step-pair.decode-pair-b64-cache1152.pmc.txt",
+                                    "hbm_bytes_per_step")},
                    "warm": {"steps_per_s": 1e3 / ms_dec, "ms_per_step": ms_dec,
                             "hbm_frac": dbytes / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                             "note": "back-to-back steps; the 222 MB of the pair stay in the "
