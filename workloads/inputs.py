@@ -78,6 +78,31 @@ def prefill_inputs(shape: MixerShape, seed=0, layer: int | None = None) -> dict:
     return out
 
 
+_ROW_KEYS = ("q", "k", "v", "x", "delta", "Bm", "Cm", "z")
+_PARAM_KEYS = ("A", "D", "conv_w", "conv_b", "beta_a", "beta_s")
+
+
+def cached_meta_inputs(shape: MixerShape, seed=0):
+    """Inputs for a prefill whose meta rows are cached.  The meta rows are the
+    same for every sequence (batch 0's first M rows of ``prefill_inputs``).
+
+    Returns (full, tokens, meta): ``full`` is the whole [B, M + N] input with
+    those shared meta rows, ``tokens`` its last N rows (plus the parameters),
+    ``meta`` the M meta rows of one sequence ([M, ...], plus the parameters).
+    """
+    full = prefill_inputs(shape, seed)
+    M = shape.M
+    for key in _ROW_KEYS:
+        full[key] = np.ascontiguousarray(full[key])
+        full[key][:, :M] = full[key][0:1, :M]
+    tokens = {key: np.ascontiguousarray(full[key][:, M:]) for key in _ROW_KEYS}
+    meta = {key: np.ascontiguousarray(full[key][0, :M]) for key in _ROW_KEYS}
+    for key in _PARAM_KEYS:
+        tokens[key] = full[key]
+        meta[key] = full[key]
+    return full, tokens, meta
+
+
 def decode_inputs(shape: MixerShape, seed=0) -> dict:
     """Inputs of one decode token through an adjacent pair of layers.
 
