@@ -54,7 +54,8 @@ class PrefillArgs(ctypes.Structure):
                             "conv_b", "beta_a", "beta_s", "ya", "ys", "out", "conv_state_out",
                             "h_out", "kv")] + [("kv_bytes", _sz), ("kv_reuse", _i),
                                                ("stream2", _vp), ("workspace", _vp),
-                                               ("workspace_bytes", _sz)]
+                                               ("workspace_bytes", _sz)] + [
+        (n, _vp) for n in ("meta_k", "meta_v", "conv_state_in", "h0")]
 
 
 class StepArgs(ctypes.Structure):

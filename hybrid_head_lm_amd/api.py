@@ -187,10 +187,13 @@ class PrefillPlan:
     def __init__(self, t: dict, n_meta: int, window: int, rope_base: float = 10000.0,
                  eps: float = 1e-6, pos0: int = 0, scale: float = 0.0, want_states=True,
                  out=None, ya=None, ys=None, workspace=None, kv=None, kv_reuse=False,
-                 stream2=None):
+                 stream2=None, meta=None, conv_state_in=None, h0=None):
         """kv: prepared K/V buffer (allocated here when None).  kv_reuse: read
         kv as prepared by an earlier layer (t["k"], t["v"] are then unused).
-        stream2: a torch stream on which the SSM branch runs concurrently."""
+        stream2: a torch stream on which the SSM branch runs concurrently.
+        meta: cached meta tokens, {"k": [n_meta, Hkv, Dh], "v": ...}; t then
+        holds the real-token rows only.  conv_state_in [B, Di, K-1], h0
+        [B, Di, N]: SSM-branch states entering the rows (float32)."""
         q = t["q"]
         dev = _dev(*[t[k] for k in ("q", "x", "delta", "Bm", "Cm", "z", "A", "D",
                                      "conv_w", "conv_b", "beta_a", "beta_s")])
@@ -218,8 +221,20 @@ class PrefillPlan:
             setattr(a, k, t[k].data_ptr())
         if not kv_reuse:
             a.k, a.v = t["k"].data_ptr(), t["v"].data_ptr()
+        if meta is not None:
+            _dev(meta["k"], meta["v"])
+            a.meta_k, a.meta_v = meta["k"].data_ptr(), meta["v"].data_ptr()
+        _dev(conv_state_in, h0)
+        if conv_state_in is not None:
+            _f32(conv_state_in)
+            a.conv_state_in = conv_state_in.data_ptr()
+        if h0 is not None:
+            _f32(h0)
+            a.h0 = h0.data_ptr()
+        self._keep = (meta, conv_state_in, h0)
+        key_rows = T + (n_meta if meta is not None else 0)
         if kv is None:
-            kv = _ws(lib.hm_attn_kv_bytes(B, T, Hkv, Dh, dtype_code(q)), dev)
+            kv = _ws(lib.hm_attn_kv_bytes(B, key_rows, Hkv, Dh, dtype_code(q)), dev)
         self.kv = kv
         a.kv, a.kv_bytes, a.kv_reuse = kv.data_ptr(), kv.numel() * kv.element_size(), int(kv_reuse)
         self.stream2 = stream2

@@ -68,10 +68,16 @@ const char* hm_last_error(void) { return hm::g_last_error.c_str(); }
 
 // Workspace of one prefill layer: the scan scratch, then (when the caller gives
 // no kv buffer) the prepared K/V, each 256-byte aligned.
+// Rows of prepared K/V: the meta rows come first when they are cached.
+static int prefill_key_rows(const hm_prefill_args* a) {
+  return a->T + ((a->meta_k != nullptr || a->meta_v != nullptr) ? a->n_meta : 0);
+}
+
 size_t hm_mixer_prefill_workspace(const hm_prefill_args* a) {
   if (!a) return 0;
   size_t ws = hm::align_up(hm_selective_scan_workspace(a->B, a->T, a->Di, a->N), 256);
-  if (a->kv == nullptr) ws += hm::align_up(hm_attn_kv_bytes(a->B, a->T, a->Hkv, a->Dh, a->dtype), 256);
+  if (a->kv == nullptr)
+    ws += hm::align_up(hm_attn_kv_bytes(a->B, prefill_key_rows(a), a->Hkv, a->Dh, a->dtype), 256);
   return ws;
 }
 
@@ -84,6 +90,16 @@ hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream) {
   HM_REQUIRE(a->ya != a->ys && a->ya != a->out && a->ys != a->out, HM_ERR_INVALID,
              "ya, ys and out must be distinct buffers");
   HM_REQUIRE(!a->kv_reuse || a->kv != nullptr, HM_ERR_INVALID, "kv_reuse needs a kv buffer");
+  const bool cached_meta = a->meta_k != nullptr || a->meta_v != nullptr;
+  if (cached_meta) {
+    HM_PTR(a->meta_k);
+    HM_PTR(a->meta_v);
+    HM_REQUIRE(a->n_meta > 0, HM_ERR_INVALID, "cached meta tokens need n_meta > 0");
+    HM_REQUIRE(hm::prefill_fusable(a), HM_ERR_UNSUPPORTED,
+               "cached meta tokens need bf16, Dh = 64, N = 16, K = 4, a width that is a "
+               "multiple of 8, 16-byte aligned rows and no stream2");
+  }
+  const int Tk = prefill_key_rows(a);   // key rows (prepared K/V)
   const size_t need = hm_mixer_prefill_workspace(a);
   HM_REQUIRE(a->workspace != nullptr && a->workspace_bytes >= need && hm::aligned16(a->workspace),
              HM_ERR_WORKSPACE, "workspace smaller than hm_mixer_prefill_workspace()");
@@ -105,17 +121,19 @@ hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream) {
       s = hm::fork_join(st, st2, /*fork=*/true);
       if (s != HM_OK) return s;
     }
+    // (with cached meta tokens only the fused path runs; the parts are then
+    // validated against the key rows, which include the meta rows)
     if (!a->kv_reuse) {
-      s = hm::attn_kv_prepare_impl(a->k, a->v, kv, kvb, a->B, a->T, a->Hkv, a->Dh, a->rope_base,
+      s = hm::attn_kv_prepare_impl(a->k, a->v, kv, kvb, a->B, Tk, a->Hkv, a->Dh, a->rope_base,
                                    a->pos0, a->dtype, st, dry);
       if (s != HM_OK) return s;
     }
-    s = hm::attn_with_kv_impl(a->q, kv, kvb, a->ya, a->B, a->T, a->Hq, a->Hkv, a->Dh, a->n_meta,
+    s = hm::attn_with_kv_impl(a->q, kv, kvb, a->ya, a->B, Tk, a->Hq, a->Hkv, a->Dh, a->n_meta,
                               a->window, a->rope_base, a->pos0, a->scale, a->dtype, st, dry);
     if (s != HM_OK) return s;
-    s = hm::conv_scan_impl(a->x, a->conv_w, a->conv_b, nullptr, a->conv_state_out, a->delta,
-                           a->A, a->Bm, a->Cm, a->D, a->z, nullptr, a->ys, a->h_out, a->B,
-                           a->T, a->Di, a->K, a->N, a->dtype, ws, wscan, st2,
+    s = hm::conv_scan_impl(a->x, a->conv_w, a->conv_b, a->conv_state_in, a->conv_state_out,
+                           a->delta, a->A, a->Bm, a->Cm, a->D, a->z, a->h0, a->ys, a->h_out,
+                           a->B, a->T, a->Di, a->K, a->N, a->dtype, ws, wscan, st2,
                            /*fuse_conv=*/true, dry);
     if (s != HM_OK) return s;
     if (!dry && st2 != st) {

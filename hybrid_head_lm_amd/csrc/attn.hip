@@ -34,8 +34,8 @@ namespace {
 __global__ __launch_bounds__(64) void attn_prep_bf16(
     const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, bf16_t* __restrict__ Kr,
     bf16_t* __restrict__ Vt, int T, int Tpad, int Hkv, long long pos0, double rstep) {
-  attn_prep_bf16_body(blockIdx.x, blockIdx.y, blockIdx.z, k, v, Kr, Vt, T, Tpad, Hkv, pos0,
-                      rstep);
+  attn_prep_bf16_body(blockIdx.x, blockIdx.y, blockIdx.z, k, v, nullptr, nullptr, 0, Kr, Vt, T,
+                      Tpad, Hkv, pos0, rstep);
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn_fwd_bf16(
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     float qscale, double rstep, int n_qt, int n_groups) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages][2][8192];
   attn_fwd_bf16_body(smem, blockIdx.x, q, Kr, Vt, o, T, Tpad, Hq, Hkv, M, W, pos0, qscale, rstep,
-                     n_qt, n_groups);
+                     n_qt, n_groups, T, 0);
 }
 
 // ---------------------------------------------------------------- float32 path

@@ -37,11 +37,15 @@ HM_DEV void rot_rev(long long pos, double theta_rev, float* s, float* c) {
 }
 
 // One 64-thread workgroup per (quarter of a 64-key tile, KV head, batch): it
-// rotates 16 K rows and writes 16 rows (dims) of the transposed V tile.
+// rotates 16 K rows and writes 16 rows (dims) of the transposed V tile.  Key
+// row j < Mk comes from the cached meta rows meta_k / meta_v [Mk, Hkv, 64]
+// (shared by the batch), key row Mk + i from row i of k / v [B, T, Hkv, 64].
 HM_DEV void attn_prep_bf16_body(int bx, int g, int b, const bf16_t* __restrict__ k,
-                                const bf16_t* __restrict__ v, bf16_t* __restrict__ Kr,
-                                bf16_t* __restrict__ Vt, int T, int Tpad, int Hkv,
-                                long long pos0, double rstep) {
+                                const bf16_t* __restrict__ v,
+                                const bf16_t* __restrict__ meta_k,
+                                const bf16_t* __restrict__ meta_v, int Mk,
+                                bf16_t* __restrict__ Kr, bf16_t* __restrict__ Vt, int T,
+                                int Tpad, int Hkv, long long pos0, double rstep) {
   __shared__ __attribute__((aligned(16))) bf16_t sv[64][16 + 2];
   const int part = bx & 3, tile = bx >> 2;
   const int t = threadIdx.x;
@@ -50,8 +54,9 @@ HM_DEV void attn_prep_bf16_body(int bx, int g, int b, const bf16_t* __restrict__
     const int r = 16 * part + (t >> 2), c = t & 3;
     const int j = j0 + r;
     uint4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-    if (j < T) {
-      const bf16_t* src = k + (((size_t)b * T + j) * Hkv + g) * 64;
+    if (j < Mk + T) {
+      const bf16_t* src = j < Mk ? meta_k + ((size_t)j * Hkv + g) * 64
+                                 : k + (((size_t)b * T + (j - Mk)) * Hkv + g) * 64;
       uint4 xl = *(const uint4*)(src + 8 * c);
       uint4 xh = *(const uint4*)(src + 32 + 8 * c);
       const bf16_t* pl = (const bf16_t*)&xl;
@@ -81,8 +86,10 @@ HM_DEV void attn_prep_bf16_body(int bx, int g, int b, const bf16_t* __restrict__
   {  // V: dims 16 part .. +15 of the 64 keys (zero past T), written out transposed
     const int j = j0 + t;
     uint4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-    if (j < T) {
-      const bf16_t* src = v + (((size_t)b * T + j) * Hkv + g) * 64 + 16 * part;
+    if (j < Mk + T) {
+      const bf16_t* src = (j < Mk ? meta_v + ((size_t)j * Hkv + g) * 64
+                                  : v + (((size_t)b * T + (j - Mk)) * Hkv + g) * 64) +
+                          16 * part;
       v0 = *(const uint4*)src;
       v1 = *(const uint4*)(src + 8);
     }
@@ -123,10 +130,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 // A workgroup of 4 waves owns 128 query rows of one head (32 per wave) and
 // walks the key tiles visible from them: the meta tiles, then the window.
 // smem: the workgroup's kStages x 2 x 8 KB of LDS (K and V^T tile per stage).
+// Tk key rows (prepared K/V); the Tq query rows of q and o are rows
+// qoff .. qoff + Tq - 1 of X~ (qoff = 0 unless the meta rows are cached).
 HM_DEV void attn_fwd_bf16_body(
-    unsigned char (*smem)[2][8192], int bid, const bf16_t* __restrict__ q, const bf16_t* __restrict__ Kr,
-    const bf16_t* __restrict__ Vt, bf16_t* __restrict__ o, int T, int Tpad, int Hq, int Hkv,
-    int M, int W, long long pos0, float qscale, double rstep, int n_qt, int n_groups) {
+    unsigned char (*smem)[2][8192], int bid, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ Kr, const bf16_t* __restrict__ Vt, bf16_t* __restrict__ o, int Tk,
+    int Tpad, int Hq, int Hkv, int M, int W, long long pos0, float qscale, double rstep, int n_qt,
+    int n_groups, int Tq, int qoff) {
   // Work item.  A group is (query tile, b, kv head) and its items are the
   // Hq/Hkv query heads that read the same K/V.  Groups are ranked heaviest
   // first (the visible key count never decreases with the query tile), rank r
@@ -148,16 +158,17 @@ HM_DEV void attn_fwd_bf16_body(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, gq = lane >> 5;
-  const int i0 = qt * kBM, i1 = min(i0 + kBM, T);
-  const int wi0 = i0 + wave * kWR, wi1 = min(wi0 + kWR, T);
-  const int qrow = min(wi0 + n, T - 1);
+  const int qend = qoff + Tq;                   // one past the last query row of X~
+  const int i0 = qoff + qt * kBM, i1 = min(i0 + kBM, qend);
+  const int wi0 = i0 + wave * kWR, wi1 = min(wi0 + kWR, qend);
+  const int qrow = min(wi0 + n, qend - 1);
 
   // Q fragment (B operand of S^T = K Q^T): lane holds query qrow, dims
   // 16 s + 8 gq + e.  Rotated in float32, scaled by scale*log2(e), rounded to
   // bf16.  theta_d / 2 pi = rstep^d / 2 pi by double-precision products.
   bf16x8_v qf[4];
   {
-    const bf16_t* src = q + (((size_t)b * T + qrow) * Hq + h) * 64;
+    const bf16_t* src = q + (((size_t)b * Tq + (qrow - qoff)) * Hq + h) * 64;
     float xs[4][8];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -247,7 +258,7 @@ HM_DEV void attn_fwd_bf16_body(
     __syncthreads();
     if (it + 1 < ntiles) issue(it + 1);
     const int j0 = tile_at(it) * kBN;
-    const int cls = hm_tile_class(wi0, wi1, j0, min(j0 + kBN, T), M, W);
+    const int cls = hm_tile_class(wi0, wi1, j0, min(j0 + kBN, Tk), M, W);
     if (cls == 0) continue;
     // S^T - m_ref (accumulated onto -m_ref); the two 32-key blocks are
     // independent accumulation chains, alternated
@@ -265,7 +276,7 @@ HM_DEV void attn_fwd_bf16_body(
         S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             *(const bf16x8_v*)(sk + lds_off(kb * 32 + n, 2 * k4 + gq)), qf[k4], S[kb], 0, 0, 0);
     __builtin_amdgcn_s_setprio(0);
-    if (cls == 1 || j0 + kBN > T) {
+    if (cls == 1 || j0 + kBN > Tk) {
       // element (kb, i) is key kbase + off with off = 32 kb + 16 (i / 8) + i % 8;
       // visible iff off <= a and (off < mm or off >= w)  (hm_visible, shifted)
       const int kbase = j0 + 8 * gq;
@@ -336,9 +347,9 @@ HM_DEV void attn_fwd_bf16_body(
   }
 
   const float l = l_run + __shfl_xor(l_run, 32);
-  if (qi < T) {
+  if (qi < qend) {
     const float inv = 1.f / l;
-    bf16_t* dst = o + (((size_t)b * T + qi) * Hq + h) * 64;
+    bf16_t* dst = o + (((size_t)b * Tq + (qi - qoff)) * Hq + h) * 64;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll

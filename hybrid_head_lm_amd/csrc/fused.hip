@@ -25,6 +25,8 @@ struct PrepGeom {
   int n;       // workgroups (0: K/V already prepared)
   int tiles4;  // Tpad / 16
   int Hkv;
+  int Mk;      // cached meta rows in front of the T token rows (0: none)
+  const bf16_t *meta_k, *meta_v;
 };
 struct AggGeom {
   int n;       // workgroups = gx * (nC - 1) * B
@@ -36,13 +38,14 @@ __global__ __launch_bounds__(64) void prefill_prep_agg(
     bf16_t* __restrict__ Kr, bf16_t* __restrict__ Vt, int Tpad, long long pos0, double rstep,
     AggGeom ag, const bf16_t* __restrict__ x, const bf16_t* __restrict__ dl,
     const float* __restrict__ A, const bf16_t* __restrict__ Bm, const float* __restrict__ cw,
-    const float* __restrict__ cb, float* __restrict__ E, float* __restrict__ S, int T, int Di,
-    int L, int nC) {
+    const float* __restrict__ cb, const float* __restrict__ cst_in, float* __restrict__ E,
+    float* __restrict__ S, int T, int Di, int L, int nC) {
   int bid = blockIdx.x;
   if (bid < pg.n) {
     const int bx = bid % pg.tiles4, g = (bid / pg.tiles4) % pg.Hkv;
     const int b = bid / (pg.tiles4 * pg.Hkv);
-    attn_prep_bf16_body(bx, g, b, k, v, Kr, Vt, T, Tpad, pg.Hkv, pos0, rstep);
+    attn_prep_bf16_body(bx, g, b, k, v, pg.meta_k, pg.meta_v, pg.Mk, Kr, Vt, T, Tpad, pg.Hkv,
+                        pos0, rstep);
     return;
   }
   bid -= pg.n;
@@ -50,7 +53,7 @@ __global__ __launch_bounds__(64) void prefill_prep_agg(
   // (the aggregate pass reads neither C, D, z nor writes y: B stands in for C)
   __shared__ ScanLds<bf16_t, false> sm;
   scan_chunk_body<bf16_t, true, false, true>(&sm, nullptr, gxi, kc, b, x, dl, A, Bm, Bm, nullptr,
-                                              nullptr, cw, cb, nullptr, nullptr, E, S, nullptr,
+                                              nullptr, cw, cb, cst_in, nullptr, E, S, nullptr,
                                               nullptr, T, Di, L, nC);
 }
 
@@ -74,17 +77,18 @@ prefill_attn_final(int n_attn, const bf16_t* __restrict__ q, const bf16_t* __res
                    const bf16_t* __restrict__ Bm, const bf16_t* __restrict__ Cm,
                    const float* __restrict__ D, const bf16_t* __restrict__ z,
                    const float* __restrict__ cw, const float* __restrict__ cb,
-                   float* __restrict__ cst_out, float* __restrict__ E, float* __restrict__ S,
+                   const float* __restrict__ cst_in, float* __restrict__ cst_out,
+                   const float* __restrict__ h0, float* __restrict__ E, float* __restrict__ S,
                    bf16_t* __restrict__ y, float* __restrict__ h_out, int T, int Di, int L,
-                   int nC) {
+                   int nC, int Mk) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kAttnLds];
   // The final-pass workgroups take the low ids (dispatched first), the latest
   // chunks (longest own carry) first; the attention workgroups follow.
   const int n_fin = (int)gridDim.x - n_attn;
   int bid = blockIdx.x;
   if (bid >= n_fin) {
-    attn_fwd_bf16_body((unsigned char(*)[2][8192])smem, bid - n_fin, q, Kr, Vt, o, T, Tpad, Hq,
-                       Hkv, M, W, pos0, qscale, rstep, n_qt, n_groups);
+    attn_fwd_bf16_body((unsigned char(*)[2][8192])smem, bid - n_fin, q, Kr, Vt, o, Mk + T, Tpad,
+                       Hq, Hkv, M, W, pos0, qscale, rstep, n_qt, n_groups, T, Mk);
     return;
   }
   bid = n_fin - 1 - bid;
@@ -98,13 +102,17 @@ prefill_attn_final(int n_attn, const bf16_t* __restrict__ q, const bf16_t* __res
 
   // 1. Chunk kk < nC-1 maps the state h to exp2(a2 * S_kk) h + E_kk (sum of
   //    delta, end state from a zero start).  Composing the maps of chunks
-  //    0 .. kk-1 from h = 0 gives the state entering chunk kk.  Wave w
-  //    composes states 4w .. 4w+3 of the 64 channels up to the workgroup's
-  //    last chunk and keeps the states entering each of its chunks.
+  //    0 .. kk-1 from the initial state h0 (or zero) gives the state entering
+  //    chunk kk.  Wave w composes states 4w .. 4w+3 of the 64 channels up to
+  //    the workgroup's last chunk and keeps the states entering each of its
+  //    chunks.
   {
-    float a2[4], H[4] = {0.f, 0.f, 0.f, 0.f};
+    float a2[4], H[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) a2[e] = A[c * kNS + 4 * wave + e] * kLog2e;
+    for (int e = 0; e < 4; ++e) {
+      a2[e] = A[c * kNS + 4 * wave + e] * kLog2e;
+      H[e] = h0 ? h0[((size_t)b * Di + c) * kNS + 4 * wave + e] : 0.f;
+    }
     const int kend = min(k0 + kChunkWaves, nC) - 1;   // compose chunks 0 .. kend-1
     const float* ep = E + ((size_t)b * nC * kNS + 4 * wave) * Di + c;
     const float* sp = S + (size_t)b * nC * Di + c;
@@ -140,7 +148,7 @@ prefill_attn_final(int n_attn, const bf16_t* __restrict__ q, const bf16_t* __res
   // 3. The chunk itself, in this wave's 8 KB of the (idle) attention ring.
   scan_chunk_body<bf16_t, true, true, true, true>(
       (ScanLds<bf16_t, true>*)(smem + wave * 8192), h, gxi, k, b, x, dl, A, Bm, Cm, D, z, cw, cb,
-      nullptr, cst_out, E, S, y, h_out, T, Di, L, nC);
+      cst_in, cst_out, E, S, y, h_out, T, Di, L, nC);
 }
 
 }  // namespace
@@ -150,13 +158,15 @@ namespace hm {
 bool prefill_fusable(const hm_prefill_args* a) {
   return a->dtype == HM_BF16 && a->stream2 == nullptr && a->Dh == 64 && a->N == kNS &&
          a->K == kConvK && a->Di % 8 == 0 && aligned16(a->x) && aligned16(a->delta) &&
-         aligned16(a->Bm) && aligned16(a->Cm) && (a->z == nullptr || aligned16(a->z));
+         aligned16(a->Bm) && aligned16(a->Cm) && (a->z == nullptr || aligned16(a->z)) &&
+         (a->meta_k == nullptr || (aligned16(a->meta_k) && aligned16(a->meta_v)));
 }
 
 // Arguments were validated by the caller (the unfused parts in dry-run mode).
 hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, hipStream_t st) {
   const int B = a->B, T = a->T, Di = a->Di, Hq = a->Hq, Hkv = a->Hkv;
-  const int Tpad = (T + 63) / 64 * 64;
+  const int Mk = a->meta_k ? a->n_meta : 0;     // cached meta rows in front of the tokens
+  const int Tpad = (Mk + T + 63) / 64 * 64;     // prepared key rows
   bf16_t* Kr = (bf16_t*)kv;
   bf16_t* Vt = Kr + (size_t)B * Hkv * Tpad * 64;
   const double l2b = log2((double)a->rope_base);
@@ -170,18 +180,20 @@ hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, 
   const int gx = (Di + 63) / 64;
 
   // 1. K/V pre-pass | chunk aggregates (chunks 0 .. nC-2)
-  PrepGeom pg{a->kv_reuse ? 0 : (Tpad / 16) * Hkv * B, Tpad / 16, Hkv};
+  PrepGeom pg{a->kv_reuse ? 0 : (Tpad / 16) * Hkv * B, Tpad / 16, Hkv, Mk,
+              (const bf16_t*)a->meta_k, (const bf16_t*)a->meta_v};
   AggGeom ag{gx * (nC - 1) * B, gx, nC > 1 ? nC - 1 : 1};
   if (pg.n + ag.n > 0) {
     hipLaunchKernelGGL(prefill_prep_agg, dim3(pg.n + ag.n), dim3(64), 0, st, pg,
                        (const bf16_t*)a->k, (const bf16_t*)a->v, Kr, Vt, Tpad, a->pos0, rstep,
                        ag, (const bf16_t*)a->x, (const bf16_t*)a->delta, a->A,
-                       (const bf16_t*)a->Bm, a->conv_w, a->conv_b, E, S, T, Di, L, nC);
+                       (const bf16_t*)a->Bm, a->conv_w, a->conv_b, a->conv_state_in, E, S, T,
+                       Di, L, nC);
     hm_status s = check_launch("prefill_prep_agg");
     if (s != HM_OK) return s;
   }
   // 2. attention | final scan pass
-  const int n_qt = (T + 128 - 1) / 128;
+  const int n_qt = (T + kBM - 1) / kBM;          // query tiles over the token rows
   const int n_groups = B * Hkv * n_qt;
   const int n_attn = 8 * ((n_groups + 7) / 8) * (Hq / Hkv);
   const FinalGeom fg{gx, (nC + kChunkWaves - 1) / kChunkWaves};
@@ -191,8 +203,8 @@ hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, 
                      Tpad, Hq, Hkv, a->n_meta, a->window, a->pos0, scale * kLog2e, rstep, n_qt,
                      n_groups, fg, (const bf16_t*)a->x, (const bf16_t*)a->delta, a->A,
                      (const bf16_t*)a->Bm, (const bf16_t*)a->Cm, a->D, (const bf16_t*)a->z,
-                     a->conv_w, a->conv_b, a->conv_state_out, E, S, (bf16_t*)a->ys, a->h_out, T,
-                     Di, L, nC);
+                     a->conv_w, a->conv_b, a->conv_state_in, a->conv_state_out, a->h0, E, S,
+                     (bf16_t*)a->ys, a->h_out, T, Di, L, nC, Mk);
   hm_status s = check_launch("prefill_attn_final");
   if (s != HM_OK) return s;
   // 3. branch norm and average

@@ -177,6 +177,22 @@ hm_status hm_branch_norm_mean(const void* ya, const void* ys, const float* beta_
  * shapes, dtype and kv as the call.  Layers that run one after the other on
  * one stream may share one workspace, and a layer with kv_reuse may take its
  * kv from the workspace of the layer that prepared it.
+ * SSM-branch initial states (optional, f32): conv_state_in [B, Di, K-1] (the
+ * K-1 inputs x before the first row, oldest first) and h0 [B, Di, N]; NULL
+ * means zeros.
+ * Cached meta tokens (optional; Hymba blog, "Hymba 的整体架构": the meta tokens
+ * are learned constants prepended to every input, so in a given layer their K
+ * and V and the SSM-branch states after them do not depend on the prompt):
+ * meta_k, meta_v [n_meta, Hkv, Dh] (act dtype, pre-RoPE, shared by the batch)
+ * are the meta rows' K and V.  q, k, v, x, delta, Bm, Cm, z then hold only the
+ * T real tokens, which are rows n_meta + i of X~ (positions pos0 + n_meta + i)
+ * and attend to the meta rows and to each other under the usual visibility;
+ * ya, ys, out are [B, T, Di]; conv_state_in and h0 should then hold the
+ * states after the meta rows (as conv_state_out and h_out of a call over the
+ * meta rows alone return them).  The prepared K/V (kv, or the workspace)
+ * covers n_meta + T rows: hm_attn_kv_bytes(B, n_meta + T, Hkv, Dh, dtype).
+ * Supported for bf16 with Dh = 64 on one stream (no stream2); otherwise
+ * HM_ERR_UNSUPPORTED.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int B, T, Hq, Hkv, Dh, Di, N, K, n_meta, window;
@@ -195,6 +211,8 @@ typedef struct {
   void* stream2;                              /* optional second stream */
   void* workspace;
   size_t workspace_bytes;
+  const void *meta_k, *meta_v;                /* optional [n_meta, Hkv, Dh], see below */
+  const float *conv_state_in, *h0;            /* optional [B, Di, K-1], [B, Di, N] */
 } hm_prefill_args;
 hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream);
 size_t hm_mixer_prefill_workspace(const hm_prefill_args* a);

@@ -129,6 +129,31 @@ def test_step_and_prefill_reject_bad_arguments():
     assert L.hm_mixer_prefill(None, None) == hm.HM_ERR_INVALID
 
 
+def test_prefill_cached_meta_rejects_unsupported_modes():
+    """Cached meta tokens run only on the fused bf16 path: f32, a second
+    stream or a missing meta_v are refused before anything is launched."""
+    L = hm.lib
+    p = hm.PrefillArgs(B=1, T=64, Hq=2, Hkv=1, Dh=64, Di=128, N=16, K=4, n_meta=4, window=16,
+                       rope_base=1e4, eps=1e-6, dtype=hm.HM_BF16)
+    for i, name in enumerate(("ya", "ys", "out")):
+        setattr(p, name, FAKE.value + 4096 * i)
+    p.meta_k = FAKE
+    assert L.hm_mixer_prefill(ctypes.byref(p), None) == hm.HM_ERR_INVALID   # meta_v missing
+    p.meta_v = FAKE
+    p.n_meta = 0
+    assert L.hm_mixer_prefill(ctypes.byref(p), None) == hm.HM_ERR_INVALID   # no meta rows
+    p.n_meta = 4
+    p.dtype = hm.HM_F32
+    assert L.hm_mixer_prefill(ctypes.byref(p), None) == hm.HM_ERR_UNSUPPORTED
+    p.dtype = hm.HM_BF16
+    p.stream2 = FAKE
+    assert L.hm_mixer_prefill(ctypes.byref(p), None) == hm.HM_ERR_UNSUPPORTED
+    # the prepared K/V covers the meta rows too
+    p.stream2 = None
+    n_plain = L.hm_mixer_prefill_workspace(ctypes.byref(p))
+    assert n_plain >= L.hm_attn_kv_bytes(1, 68, 1, 64, hm.HM_BF16)
+
+
 def test_ctypes_structs_match_the_header(tmp_path):
     """The binding's hm_prefill_args / hm_step_args layouts equal the C ones."""
     import shutil

@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import GLOBAL_PREFILL, SWA_PREFILL, TINY, prefill_inputs, with_
+from workloads import (GLOBAL_PREFILL, SWA_PREFILL, TINY, cached_meta_inputs, prefill_inputs,
+                       with_)
 
 pytestmark = pytest.mark.gpu
 
@@ -274,3 +275,63 @@ def test_mixer_prefill_two_streams_and_kv_reuse(dtype):
         ref = oracle.mixer_prefill(src, shape.M, shape.W)
         for k, got in (("ya", plan.ya), ("ys", plan.ys), ("out", plan.out), ("ssm_state", plan.h)):
             assert_close(down(got), ref[k], dtype, f"{k}")
+
+
+# ------------------------------------------------------------------ cached meta tokens
+def _cached_meta_run(shape, seed, cache=None):
+    """Prefill of the real tokens with the meta rows cached, against the
+    oracle's cached-meta prefill (itself pinned against the full prefill)."""
+    full, tokens, meta = cached_meta_inputs(shape, seed)
+    if cache is None:
+        cache = oracle.meta_cache(meta)
+        # the GPU takes the states in float32
+        cache["ssm_state"] = cache["ssm_state"].astype(np.float32).astype(np.float64)
+    B = shape.B
+    t = up_inputs(tokens, "bf16")
+    mk = up(meta["k"], "bf16")
+    mv = up(meta["v"], "bf16")
+    cs = up(np.broadcast_to(cache["conv_state"], (B,) + cache["conv_state"].shape).copy(), "f32")
+    h0 = up(np.broadcast_to(cache["ssm_state"], (B,) + cache["ssm_state"].shape).copy(), "f32")
+    plan = hm.PrefillPlan(t, shape.M, shape.W, meta={"k": mk, "v": mv}, conv_state_in=cs, h0=h0)
+    plan.run()
+    torch.cuda.synchronize()
+    ref = oracle.mixer_prefill_cached_meta(tokens, cache, shape.M, shape.W)
+    return plan, ref
+
+
+@pytest.mark.parametrize("B,M,N,W,Hq,Hkv", [(1, 128, 2048, 1024, 25, 5), (2, 5, 77, 32, 4, 2),
+                                            (3, 16, 300, 0, 5, 1), (1, 4, 20, 16, 5, 5),
+                                            (2, 130, 40, 64, 10, 5), (1, 64, 1, 32, 2, 1)])
+def test_mixer_prefill_bf16_cached_meta(B, M, N, W, Hq, Hkv):
+    """Only the real tokens computed, the meta rows' K/V and the SSM-branch
+    states after them taken from a cache: short and ragged token counts, meta
+    counts off the tile grid, several sequences, global attention."""
+    shape = with_(SWA_PREFILL, B=B, M=M, N=N, W=W, Hq=Hq, Hkv=Hkv, Di=Hq * 64)
+    plan, ref = _cached_meta_run(shape, 40 + N)
+    for k, got in (("ya", plan.ya), ("ys", plan.ys), ("out", plan.out), ("ssm_state", plan.h)):
+        assert_close(down(got), ref[k], "bf16", f"cached meta {k}")
+    assert np.array_equal(down(plan.conv_state), ref["conv_state"])
+
+
+def test_mixer_prefill_cached_meta_states_from_the_library():
+    """The documented workflow: the meta rows alone through hm_mixer_prefill
+    (one sequence) give the states; the cached prefill of the tokens then
+    equals the last rows of the full prefill over [meta; tokens]."""
+    shape = with_(SWA_PREFILL, B=2, M=32, N=200, W=64, Hq=5, Hkv=1, Di=320)
+    full, tokens, meta = cached_meta_inputs(shape, 9)
+    mshape = with_(shape, B=1, N=0)
+    mt = up_inputs({k: (v[None] if k in ("q", "k", "v", "x", "delta", "Bm", "Cm", "z") else v)
+                    for k, v in meta.items()}, "bf16")
+    mplan = hm.PrefillPlan(mt, mshape.M, mshape.W)
+    mplan.run()
+    t = up_inputs(tokens, "bf16")
+    cs = mplan.conv_state.expand(shape.B, -1, -1).contiguous()
+    h0 = mplan.h.expand(shape.B, -1, -1).contiguous()
+    plan = hm.PrefillPlan(t, shape.M, shape.W, meta={"k": mt["k"][0], "v": mt["v"][0]},
+                          conv_state_in=cs, h0=h0)
+    plan.run()
+    torch.cuda.synchronize()
+    ref = oracle.mixer_prefill(full, shape.M, shape.W)
+    for k, got in (("ya", plan.ya), ("ys", plan.ys), ("out", plan.out), ("ssm_state", plan.h)):
+        ref_k = ref[k][:, shape.M:] if k != "ssm_state" else ref[k]
+        assert_close(down(got), ref_k, "bf16", f"cached meta via the library, {k}")
