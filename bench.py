@@ -20,8 +20,12 @@ Also reported on the same JSON line:
                 the global-attention layer (batch 4, 128 + 8192 tokens) and the
                 32-layer stack (batch 2, 128 + 16384 tokens, layers 0/15/31
                 global, adjacent sliding-window layers sharing prepared K/V);
+  cached_meta   the same layer with the meta tokens' K/V and SSM states taken
+                from a cache: only the 2048 real-token rows are computed
+                (real tokens/s, beside the full layer's real tokens/s);
   layer_step_us single-call times of the step (median, p10, p90) after the timed
-                region, and the shader clock the driver reports;
+                region, and (sclk_mhz) the shader clock the driver reports while
+                those calls run;
   ssm_branch    the conv + scan branch on its own against HBM and against the
                 non-packed fp32 VALU rate (single-pass VALU work per
                 token-channel);
@@ -162,17 +166,28 @@ def step_percentiles(fn, steps: int, while_busy=None):
 
 
 def gpu_sclk_mhz():
-    """Current shader clock from the driver's sysfs table (the line marked *),
-    or None where it cannot be read."""
+    """(current, highest level) shader clock in MHz from the driver's sysfs
+    table (the current one is the line marked *), or (None, None)."""
     import glob
     for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
         try:
+            cur, top = None, None
             for line in open(f):
+                mhz = float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+                top = mhz if top is None else max(top, mhz)
                 if line.rstrip().endswith("*"):
-                    return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+                    cur = mhz
+            return cur, top
         except (OSError, ValueError, IndexError):
             continue
-    return None
+    return None, None
+
+
+def sample_sclk(samples: list, n: int = 12, gap_s: float = 0.001):
+    """Read the current shader clock n times, gap_s apart (while the GPU works)."""
+    for _ in range(n):
+        samples.append(gpu_sclk_mhz())
+        time.sleep(gap_s)
 
 
 def cpu_model():
@@ -296,11 +311,31 @@ def main():
     # the step: one mixer layer (both branches on one stream, kernels in order)
     plan, ms = run_prefill(shape, hm, t, args.steps, args.warmup, two_streams=False)
     sclk = []
-    layer_dist = step_percentiles(plan.run, max(20, args.steps),
-                                  while_busy=lambda: sclk.append(gpu_sclk_mhz()))
-    sclk = sclk[0] if sclk else None
+    layer_dist = step_percentiles(plan.run, max(200, args.steps),
+                                  while_busy=lambda: sample_sclk(sclk))
+    cur = [c for c, _ in sclk if c is not None]
+    sclk = {"max_sampled": max(cur) if cur else None,
+            "highest_level": sclk[0][1] if sclk else None,
+            "note": "the driver's current-clock line (S:), read 12 times 1 ms apart while "
+                    "the layer calls run; it reads far below the highest level and below what "
+                    "the measured MFMA rates need, so it is an average that includes idle "
+                    "time, not the clock during the kernels"}
     _, ms_two = run_prefill(shape, hm, t, args.steps, args.warmup, two_streams=True)
     tokens = shape.B * shape.T
+
+    # the same layer with the meta tokens cached: only the N real-token rows are
+    # computed, from the meta rows' K/V and the SSM-branch states after them
+    from workloads import cached_meta_inputs
+    _, ctok, cmeta = cached_meta_inputs(shape, 0)
+    ct = to_device(ctok, shape.dtype)
+    cmk = to_device({"k": cmeta["k"], "v": cmeta["v"]}, shape.dtype)
+    cst = torch.zeros((shape.B, shape.Di, shape.K - 1), dtype=torch.float32, device="cuda")
+    ch0 = torch.zeros((shape.B, shape.Di, shape.Ns), dtype=torch.float32, device="cuda")
+    cplan = hm.PrefillPlan(ct, shape.M, shape.W, rope_base=shape.rope_base, eps=shape.eps,
+                           want_states=False, meta={"k": cmk["k"], "v": cmk["v"]},
+                           conv_state_in=cst, h0=ch0)
+    ms_cached = timed(cplan.run, args.steps, args.warmup)
+    del cplan, ct, cmk
 
     # dominant kernel on its own: attention over the prepared K/V
     ms_attn = timed(lambda: hm.attn_with_kv(t["q"], plan.kv, shape.Hkv, shape.M, shape.W,
@@ -375,8 +410,12 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "algorithmic_flop_per_launch": fl, "ms_per_launch": ms_attn},
+        "cached_meta": {"workload": shape.name + " with the 128 meta rows cached",
+                        "real_tokens_per_s": shape.B * shape.N / (ms_cached * 1e-3),
+                        "ms_per_layer": ms_cached,
+                        "full_layer_real_tokens_per_s": shape.B * shape.N / (ms * 1e-3)},
         "layer_step_us": layer_dist,
-        "sclk_mhz": sclk,     # read from the driver while the layer calls run
+        "sclk_mhz": sclk,
         "breakdown_ms": {"layer_one_stream": ms, "layer_two_streams": ms_two,
                          "attention_kernel": ms_attn, "ssm_branch": ms_ssm,
                          "norm_mean": ms_norm},
