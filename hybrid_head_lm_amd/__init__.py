@@ -65,7 +65,7 @@ class StepArgs(ctypes.Structure):
     ] + [(n, _vp) for n in ("q", "k_new", "v_new", "k_cache", "v_cache", "x", "delta", "Bm", "Cm",
                             "z", "A", "D", "conv_w", "conv_b", "conv_state", "ssm_state",
                             "beta_a", "beta_s", "out", "ya_out", "ys_out", "workspace")] + [
-        ("workspace_bytes", _sz)]
+        ("workspace_bytes", _sz), ("n_prev_seq", _vp)]
 
 
 def _load():

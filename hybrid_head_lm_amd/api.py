@@ -270,7 +270,9 @@ class StepPlan:
 
     def __init__(self, layer: dict, k_cache, v_cache, n_prev: int, n_meta: int, window: int,
                  rope_base: float = 10000.0, eps: float = 1e-6, scale: float = 0.0,
-                 want_branches=False, out=None, workspace=None):
+                 want_branches=False, out=None, workspace=None, n_prev_seq=None):
+        """n_prev_seq: optional int32 device tensor [B], one n_prev per sequence
+        (ragged batch); n_prev must then be at least its largest entry."""
         q = layer["q"]
         producer = layer.get("k_new") is not None
         dev = _dev(q, k_cache, v_cache, layer.get("k_new"), layer.get("v_new"),
@@ -299,11 +301,16 @@ class StepPlan:
             self.ya = torch.empty((B, Di), dtype=torch.float32, device=dev)
             self.ys = torch.empty((B, Di), dtype=torch.float32, device=dev)
             a.ya_out, a.ys_out = self.ya.data_ptr(), self.ys.data_ptr()
+        if n_prev_seq is not None:
+            _dev(n_prev_seq)
+            if n_prev_seq.dtype != torch.int32 or n_prev_seq.numel() != B:
+                raise TypeError("n_prev_seq must be an int32 tensor with one entry per sequence")
+            a.n_prev_seq = n_prev_seq.data_ptr()
         nb = lib.hm_mixer_step_workspace(ctypes.byref(a))
         self.ws = workspace if workspace is not None else _ws(nb, dev)
         a.workspace, a.workspace_bytes = self.ws.data_ptr(), self.ws.numel()
         self.args = a
-        self._keep = (layer, k_cache, v_cache)
+        self._keep = (layer, k_cache, v_cache, n_prev_seq)
 
     def run(self, stream=None):
         s = _stream() if stream is None else ctypes.c_void_p(stream.cuda_stream)

@@ -184,6 +184,28 @@ HM_DEV float ssm_step_one(int b, int c, int Di, const Tact* __restrict__ x,
   return ((y4[0] + y4[1]) + (y4[2] + y4[3])) * siluf_(ldx(z + idx));
 }
 
+// ---------------------------------------------------------------- per-sequence positions
+// The token of sequence b follows n_prev earlier tokens: it sits at position
+// n_meta + n_prev, its cache slot is n_meta + (n_prev mod window) (window <= 0:
+// n_meta + n_prev) and the rows 0 .. L-1 with L = n_meta + min(n_prev + 1,
+// window) are visible (all n_prev + 1 for window <= 0).  Either every sequence
+// is at n_prev_max, or nps holds one n_prev per sequence (clamped to
+// [0, n_prev_max], which the host validated against the cache size).
+struct SeqPos {
+  const int* nps;
+  int n_meta, window;
+  long long n_prev_max;
+};
+
+HM_DEV void seq_pos(const SeqPos& sp, int b, int* L, int* slot, long long* pos) {
+  long long np = sp.n_prev_max;
+  if (sp.nps) np = min(max((long long)sp.nps[b], 0ll), sp.n_prev_max);
+  const long long nv = sp.window > 0 ? min(np + 1, (long long)sp.window) : np + 1;
+  *L = (int)(sp.n_meta + nv);
+  *slot = (int)(sp.n_meta + (sp.window > 0 ? np % sp.window : np));
+  *pos = sp.n_meta + np;
+}
+
 // ---------------------------------------------------------------- bf16 attention + SSM step
 // LDS tiles of 64 cache rows x 128 bytes (K or V); the 16-byte chunk c of row r
 // sits in slot c ^ ((r >> 1) & 7), so that 16 lanes reading one chunk of 16
@@ -215,7 +237,7 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
     const float* __restrict__ D, const float* __restrict__ cw, const float* __restrict__ cb,
     float* __restrict__ conv_state, float* __restrict__ ssm_state, float* __restrict__ ys_ws,
     size_t ys_stride, float* __restrict__ part, size_t part_b_stride, int Hq, int Hkv, int Di,
-    int S, int L, int slot, long long pos, float qscale, double log2_base, double rstep,
+    int S, SeqPos sp, float qscale, double log2_base, double rstep,
     int n_split, int tiles_per_split, int ssm_per_block, int n_ssm) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecStages][2][8192];
   __shared__ float sm[4][16], sl[4][16];
@@ -225,6 +247,9 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
   const int grp = Hq / Hkv;
   const int split = blockIdx.x % n_split, pair = blockIdx.x / n_split;
   const int b = pair / Hkv, g = pair % Hkv;
+  int L, slot;
+  long long pos;
+  seq_pos(sp, b, &L, &slot, &pos);
   const size_t rs = (size_t)Hkv * 64;                       // cache row stride (elements)
   const int kt0 = split * tiles_per_split;                  // first tile of the split
   const int ntile = max(0, min(tiles_per_split, (L + 63) / 64 - kt0));
@@ -493,11 +518,14 @@ __global__ __launch_bounds__(64) void step_attn_f32(const float* __restrict__ q,
                                                     const float* __restrict__ vc,
                                                     float* __restrict__ part,
                                                     size_t part_b_stride, int B, int Hq,
-                                                    int Hkv, int S, int L, long long pos,
+                                                    int Hkv, int S, SeqPos sp,
                                                     float qscale, double log2_base) {
   const int idx = blockIdx.x * 64 + threadIdx.x;
   if (idx >= B * Hq) return;
   const int h = idx % Hq, b = idx / Hq;
+  int L, slot;
+  long long pos;
+  seq_pos(sp, b, &L, &slot, &pos);
   const int grp = Hq / Hkv, g = h / grp;
   float qr[DH];
   const float* src = q + ((size_t)b * Hq + h) * DH;
@@ -542,7 +570,7 @@ __global__ __launch_bounds__(256) void step_ssm_kv(
     float* __restrict__ conv_state, float* __restrict__ ssm_state, float* __restrict__ ys_ws,
     size_t ys_stride, int B, int Di, int n_ssm_blocks, const Tact* __restrict__ k_new,
     const Tact* __restrict__ v_new, Tact* __restrict__ k_cache, Tact* __restrict__ v_cache,
-    int Hkv, int Dh, int S, int slot, long long pos, double log2_base) {
+    int Hkv, int Dh, int S, SeqPos sp, double log2_base) {
   if ((int)blockIdx.x < n_ssm_blocks) {
     const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (long long)B * Di) return;
@@ -557,6 +585,10 @@ __global__ __launch_bounds__(256) void step_ssm_kv(
   const int d = idx % half;
   const int g = (idx / half) % Hkv;
   const int b = idx / ((long long)half * Hkv);
+  int L, slot;
+  long long pos;
+  seq_pos(sp, b, &L, &slot, &pos);
+  (void)L;
   const Tact* ks = k_new + ((size_t)b * Hkv + g) * Dh;
   const Tact* vs = v_new + ((size_t)b * Hkv + g) * Dh;
   float sn, cs;
@@ -680,8 +712,7 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
   float* ys_ws = (float*)a->workspace;
   float* part = (float*)((char*)a->workspace + g.ys_bytes);
   const int S = a->n_meta + a->cache_slots;
-  const long long pos = (long long)a->n_meta + a->n_prev;
-  const int slot = (int)hm_debug_cache_slot(a->n_prev, a->n_meta, a->window);
+  const SeqPos sp{a->n_prev_seq, a->n_meta, a->window, a->n_prev};
   const double l2b = log2((double)a->rope_base);
   const float sc = (a->scale > 0.f ? a->scale : 1.0f / sqrtf((float)a->Dh)) * kLog2e;
 
@@ -695,7 +726,7 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
                        (const bf16_t*)a->delta, (const bf16_t*)a->Bm, (const bf16_t*)a->Cm,
                        (const bf16_t*)a->z, a->A, a->D, a->conv_w, a->conv_b, a->conv_state,
                        a->ssm_state, ys_ws, g.ys_stride, part, g.part_b_stride, a->Hq, a->Hkv,
-                       a->Di, S, g.L, slot, pos, sc, l2b, exp2(-l2b / 32.0), g.n_split,
+                       a->Di, S, sp, sc, l2b, exp2(-l2b / 32.0), g.n_split,
                        g.tiles_per_split, ssm_per_block, n_ssm);
     hm_status s = hm::check_launch("step_fused_bf16");
     if (s != HM_OK) return s;
@@ -713,7 +744,7 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
                      (const float*)a->Cm, (const float*)a->z, a->A, a->D, a->conv_w, a->conv_b,
                      a->conv_state, a->ssm_state, ys_ws, g.ys_stride, a->B, a->Di, n_ssm_blocks,
                      (const float*)a->k_new, (const float*)a->v_new, (float*)a->k_cache,
-                     (float*)a->v_cache, a->Hkv, a->Dh, S, slot, pos, l2b);
+                     (float*)a->v_cache, a->Hkv, a->Dh, S, sp, l2b);
   hm_status s = hm::check_launch("step_ssm_kv");
   if (s != HM_OK) return s;
   const int nbh = (a->B * a->Hq + 63) / 64;
@@ -721,7 +752,7 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
   case DHV:                                                                                   \
     hipLaunchKernelGGL(step_attn_f32<DHV>, dim3(nbh), dim3(64), 0, st, (const float*)a->q,   \
                        (const float*)a->k_cache, (const float*)a->v_cache, part,               \
-                       g.part_b_stride, a->B, a->Hq, a->Hkv, S, g.L, pos, sc, l2b);            \
+                       g.part_b_stride, a->B, a->Hq, a->Hkv, S, sp, sc, l2b);                  \
     break;
   switch (a->Dh) {
     HM_STEP_F32(16)

@@ -234,6 +234,10 @@ size_t hm_mixer_prefill_workspace(const hm_prefill_args* a);
  * tokens (all n_prev+1 for window <= 0).  conv_state and ssm_state advance by
  * one token in place; out = branch norm-and-average of the two branches.
  * Optional ya_out / ys_out ([B, Di] f32) receive the branch outputs.
+ * Ragged batches: n_prev_seq (device int32 [B], optional) gives each sequence
+ * its own n_prev, hence its own position, slot and visible rows; n_prev must
+ * then be at least every entry (it sizes the key splits), and entries outside
+ * [0, n_prev] are clamped into it.  NULL: every sequence is at n_prev.
  * Supported: bf16 with Dh = 64 (MFMA), f32 with Dh in {16, 32, 64}; N = 16; K = 4.
  * Workspace: hm_mixer_step_workspace() bytes (per-split partials and the SSM
  * branch output).  Calls that share a workspace must not overlap (stream-
@@ -254,6 +258,7 @@ typedef struct {
   float *ya_out, *ys_out;                  /* optional [B, Di] */
   void* workspace;
   size_t workspace_bytes;
+  const int* n_prev_seq;                   /* optional [B] device int32, see below */
 } hm_step_args;
 hm_status hm_mixer_step(const hm_step_args* a, void* stream);
 size_t hm_mixer_step_workspace(const hm_step_args* a);

@@ -18,6 +18,9 @@ Readings:
 * Visible slots: the meta rows and the ring slots of the last min(n_prev+1, W)
   tokens.  Order does not matter (positions live in the rotated K).
 * The conv and SSM states advance by one token; then norm-and-average.
+* Ragged batches (``mixer_step_ragged``): the news article's limitation is a
+  property of that implementation, not of the method; every sequence is an
+  independent instance of the step above at its own n_prev.
 """
 from __future__ import annotations
 
@@ -110,3 +113,22 @@ def mixer_step(layer: dict, k_cache, v_cache, n_prev: int, n_meta: int,
     out = branch_norm_mean(ya, ys, layer["beta_a"], layer["beta_s"], eps)
     return {"out": out, "ya": ya, "ys": ys, "conv_state": conv_state,
             "ssm_state": h, "k_cache": kc, "v_cache": vc}
+
+
+_SEQ_KEYS = ("q", "k_new", "v_new", "x", "delta", "z", "Bm", "Cm", "conv_state", "ssm_state")
+
+
+def mixer_step_ragged(layer: dict, k_cache, v_cache, n_prev_seq, n_meta: int,
+                      window: int, producer: bool, rope_base: float = 10000.0,
+                      eps: float = 1e-6, scale: float = 0.0) -> dict:
+    """``mixer_step`` with one n_prev per sequence: sequence b is the step of
+    that sequence alone at n_prev_seq[b].  Same arguments and results."""
+    B = np.asarray(layer["q"]).shape[0]
+    outs = []
+    for b in range(B):
+        lb = {k: (np.asarray(v)[b:b + 1] if k in _SEQ_KEYS and v is not None else v)
+              for k, v in layer.items()}
+        outs.append(mixer_step(lb, np.asarray(k_cache)[b:b + 1], np.asarray(v_cache)[b:b + 1],
+                               int(n_prev_seq[b]), n_meta, window, producer, rope_base, eps,
+                               scale))
+    return {k: np.concatenate([o[k] for o in outs], axis=0) for k in outs[0]}

@@ -144,3 +144,53 @@ def test_decode_pair_shared_garbage_workspace():
         la["conv_state"], la["ssm_state"] = ra["conv_state"], ra["ssm_state"]
         lb["conv_state"], lb["ssm_state"] = rb["conv_state"], rb["ssm_state"]
         kc, vc = ra["k_cache"], ra["v_cache"]
+
+
+def _check_ragged(shape, nps, seed):
+    """Producer then consumer with one n_prev per sequence, against the
+    oracle's ragged step."""
+    d = decode_inputs(shape, seed)
+    t = up_inputs(d, shape.dtype)
+    kc, vc = t["k_cache"], t["v_cache"]
+    npt = torch.tensor(nps, dtype=torch.int32, device="cuda")
+    plans = [hm.StepPlan(t[name], kc, vc, shape.n_prev, shape.M, shape.W, want_branches=True,
+                         n_prev_seq=npt) for name in "ab"]
+    for p in plans:
+        p.run()
+    torch.cuda.synchronize()
+    ra = oracle.mixer_step_ragged(d["a"], d["k_cache"], d["v_cache"], nps, shape.M, shape.W,
+                                  producer=True)
+    rb = oracle.mixer_step_ragged(d["b"], ra["k_cache"], ra["v_cache"], nps, shape.M, shape.W,
+                                  producer=False)
+    dt = shape.dtype
+    for name, plan, ref in zip("ab", plans, (ra, rb)):
+        assert_close(down(plan.out), ref["out"], dt, f"{name} out")
+        assert_close(down(plan.ya), ref["ya"], dt, f"{name} ya")
+        assert_close(down(plan.ys), ref["ys"], dt, f"{name} ys")
+        assert_close(down(t[name]["ssm_state"]), ref["ssm_state"], dt, f"{name} ssm_state")
+    kcd = down(kc)
+    for b, npb in enumerate(nps):
+        slot = oracle.cache_slot(int(npb), shape.M, shape.W)
+        assert_close(kcd[b, slot], ra["k_cache"][b, slot], dt, f"written K row of sequence {b}")
+    # rows other than each sequence's own slot are untouched
+    for b, npb in enumerate(nps):
+        slot = oracle.cache_slot(int(npb), shape.M, shape.W)
+        others = [r for r in range(kcd.shape[1]) if r != slot]
+        assert np.array_equal(kcd[b, others], d["k_cache"][b, others].astype(np.float64))
+
+
+def test_decode_pair_bf16_ragged_window():
+    """Sequences before, at and after the ring wraps, in one batch."""
+    shape = with_(DECODE_PAIR, B=5, n_prev=3000)
+    _check_ragged(shape, [0, 63, 700, 1024, 3000], 31)
+
+
+def test_decode_pair_bf16_ragged_global():
+    shape = with_(DECODE_PAIR, B=3, W=0, cache_slots=256, n_prev=200, M=30)
+    _check_ragged(shape, [0, 5, 200], 32)
+
+
+@pytest.mark.parametrize("Dh", [16, 64])
+def test_decode_pair_f32_ragged(Dh):
+    shape = with_(TINY, B=3, n_prev=40, cache_slots=16, Dh=Dh, Di=2 * Dh)
+    _check_ragged(shape, [0, 15, 40], 33)

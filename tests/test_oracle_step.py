@@ -75,3 +75,28 @@ def test_valid_slots_counts():
         assert oracle.cache_slot(n, 4, 16) in s
     s = oracle.valid_slots(9, 2, 0)
     assert s.tolist() == list(range(2 + 10))
+
+
+def test_ragged_step_equals_uniform_steps():
+    """A ragged batch (one n_prev per sequence) gives each sequence exactly the
+    step of a uniform batch at its n_prev, and a uniform n_prev_seq equals the
+    scalar step."""
+    from workloads import DECODE_PAIR, decode_inputs
+    shape = with_(DECODE_PAIR, B=3, Hq=4, Hkv=2, Dh=16, Di=64, M=3, W=8, cache_slots=8,
+                  n_prev=20, dtype="f32")
+    d = decode_inputs(shape, 2)
+    nps = np.array([0, 7, 20])
+    rag = oracle.mixer_step_ragged(d["a"], d["k_cache"], d["v_cache"], nps, shape.M, shape.W,
+                                   producer=True)
+    for b, npb in enumerate(nps):
+        ref = oracle.mixer_step(d["a"], d["k_cache"], d["v_cache"], int(npb), shape.M, shape.W,
+                                producer=True)
+        for key in ("out", "ya", "ys", "conv_state", "ssm_state", "k_cache", "v_cache"):
+            np.testing.assert_allclose(rag[key][b], ref[key][b], rtol=1e-13, atol=1e-13,
+                                       err_msg=key)
+    uni = oracle.mixer_step_ragged(d["a"], d["k_cache"], d["v_cache"], np.full(3, 5), shape.M,
+                                   shape.W, producer=True)
+    ref = oracle.mixer_step(d["a"], d["k_cache"], d["v_cache"], 5, shape.M, shape.W,
+                            producer=True)
+    for key in ("out", "k_cache"):
+        np.testing.assert_allclose(uni[key], ref[key], rtol=1e-13, atol=1e-13)
