@@ -20,6 +20,7 @@ Also reported on the same JSON line:
                 the global-attention layer (batch 4, 128 + 8192 tokens) and the
                 32-layer stack (batch 2, 128 + 16384 tokens, layers 0/15/31
                 global, adjacent sliding-window layers sharing prepared K/V);
+  ragged_decode the decode pair with one n_prev per sequence (warm);
   cached_meta   the same layer with the meta tokens' K/V and SSM states taken
                 from a cache: only the 2048 real-token rows are computed
                 (real tokens/s, beside the full layer's real tokens/s);
@@ -83,14 +84,16 @@ def scan_bytes(shape) -> float:
     return 8.0 * tc + 4.0 * shape.B * shape.T * shape.Ns + 4.0 * shape.Di * (shape.Ns + 1 + 5)
 
 
-def decode_bytes(shape) -> float:
+def decode_bytes(shape, n_prev_seq=None) -> float:
     """Compulsory HBM bytes of one decode token through a producer + consumer
     layer: both read the visible cache rows (K and V), each reads and writes its
     SSM and conv states, reads q, x, delta, z, B, C and writes out; the producer
-    reads k_new, v_new and writes them into the cache."""
+    reads k_new, v_new and writes them into the cache.  n_prev_seq: one n_prev
+    per sequence (ragged batch)."""
     B, Hkv, Dh, Di, Ns = shape.B, shape.Hkv, shape.Dh, shape.Di, shape.Ns
-    vis = shape.M + (min(shape.n_prev + 1, shape.W) if shape.W > 0 else shape.n_prev + 1)
-    per_layer = (B * vis * Hkv * Dh * 2 * 2            # K and V rows
+    nps = [shape.n_prev] * B if n_prev_seq is None else list(n_prev_seq)
+    rows = sum(shape.M + (min(n + 1, shape.W) if shape.W > 0 else n + 1) for n in nps)
+    per_layer = (rows * Hkv * Dh * 2 * 2               # K and V rows
                  + B * Di * Ns * 4 * 2                 # SSM state read + write
                  + B * Di * 3 * 4 * 2                  # conv state read + write
                  + B * shape.Hq * Dh * 2               # q
@@ -388,6 +391,23 @@ def main():
     ms_dec_cold = sum(cold) / len(cold)
     del flush, flush_rd
 
+    # ragged decode: the same pair with one n_prev per sequence, uniform over
+    # 0 .. 2047 (seeded), back to back
+    import numpy as np
+    nps = np.random.default_rng(5).integers(0, 2048, size=dshape.B).astype(np.int32)
+    npt = torch.from_numpy(nps).cuda()
+    ra_plan = hm.StepPlan(d["a"], d["k_cache"], d["v_cache"], int(nps.max()), dshape.M, dshape.W,
+                          rope_base=dshape.rope_base, eps=dshape.eps, n_prev_seq=npt)
+    rb_plan = hm.StepPlan(d["b"], d["k_cache"], d["v_cache"], int(nps.max()), dshape.M, dshape.W,
+                          rope_base=dshape.rope_base, eps=dshape.eps, n_prev_seq=npt)
+
+    def ragged_step():
+        ra_plan.run()
+        rb_plan.run()
+    ms_rag = timed(ragged_step, args.steps, args.warmup)
+    rag_bytes = decode_bytes(dshape, nps)
+    del ra_plan, rb_plan
+
     result = {
         "metric": "hybrid-mixer prefill tokens/s per layer + decode steps/s; % MFMA/HBM roofline",
         "value": tokens / (ms * 1e-3),
@@ -449,6 +469,12 @@ def main():
                             "hbm_frac": dbytes / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBPS,
                             "note": "back-to-back steps; the 222 MB of the pair stay in the "
                                     "256 MB Infinity Cache"}},
+        "ragged_decode": {"workload": dshape.name + " with n_prev per sequence uniform "
+                                                    "over 0..2047 (seeded)",
+                          "steps_per_s": 1e3 / ms_rag, "ms_per_step": ms_rag,
+                          "hbm_frac": rag_bytes / (ms_rag * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                          "algorithmic_bytes_per_step": rag_bytes,
+                          "cache": "warm (back-to-back steps)"},
     }
     del pa, pb, d
 
