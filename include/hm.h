@@ -31,6 +31,8 @@
  *     no output is touched.  Errors are returned as hm_status; nothing aborts
  *     or throws across the ABI.  hm_last_error() gives a message for the last
  *     failing call on the calling thread.
+ *   - Extents (batch, rows, token counts, widths, heads) must be positive: an
+ *     empty call returns HM_ERR_INVALID and launches nothing.
  */
 #ifndef HM_H_
 #define HM_H_

@@ -178,3 +178,30 @@ def test_ctypes_structs_match_the_header(tmp_path):
     offs = vals[2:]
     assert offs[:len(fields_p)] == [getattr(hm.PrefillArgs, f).offset for f in fields_p]
     assert offs[len(fields_p):] == [getattr(hm.StepArgs, f).offset for f in fields_s]
+
+
+def test_empty_extents_are_rejected():
+    """Zero batch, rows or width: HM_ERR_INVALID from every entry point, with
+    nothing launched (the pointers are never dereferenced)."""
+    L = hm.lib
+    q, k, v, o, ws = (ctypes.c_void_p(i << 20) for i in range(1, 6))
+    for B, T in ((0, 64), (1, 0)):
+        assert L.hm_swa_meta_attn(q, k, v, o, B, T, 2, 1, 16, 0, 16, 1e4, 0, 0.0, hm.HM_F32, ws,
+                                  1 << 30, None) == hm.HM_ERR_INVALID
+        assert L.hm_causal_conv1d(q, k, None, None, o, None, B, T, 4, 4, 1, hm.HM_F32,
+                                  None) == hm.HM_ERR_INVALID
+        assert L.hm_conv_selective_scan(q, k, None, None, None, v, FAKE, FAKE, FAKE, None, None,
+                                        None, o, None, B, T, 32, 4, 16, hm.HM_F32, ws, 1 << 30,
+                                        None) == hm.HM_ERR_INVALID
+    assert L.hm_branch_norm_mean(q, k, v, FAKE, 1e-6, o, 0, 8, hm.HM_F32,
+                                 None) == hm.HM_ERR_INVALID
+    assert L.hm_branch_norm_mean(q, k, v, FAKE, 1e-6, o, 4, 0, hm.HM_F32,
+                                 None) == hm.HM_ERR_INVALID
+    p = hm.PrefillArgs(B=1, T=0, Hq=2, Hkv=1, Dh=16, Di=32, N=16, K=4, n_meta=0, window=16,
+                       rope_base=1e4, eps=1e-6, dtype=hm.HM_F32)
+    p.ya, p.ys, p.out = q.value, k.value, v.value
+    p.workspace, p.workspace_bytes = ws.value, 1 << 30
+    assert L.hm_mixer_prefill(ctypes.byref(p), None) == hm.HM_ERR_INVALID
+    s = hm.StepArgs(B=0, Hq=2, Hkv=1, Dh=16, Di=32, N=16, K=4, n_meta=4, window=16,
+                    cache_slots=16, n_prev=3, rope_base=1e4, eps=1e-6, dtype=hm.HM_F32)
+    assert L.hm_mixer_step(ctypes.byref(s), None) == hm.HM_ERR_INVALID
