@@ -27,7 +27,7 @@ EXPORTS = (
     "hm_swa_meta_attn", "hm_swa_meta_attn_workspace",
     "hm_attn_kv_bytes", "hm_attn_kv_prepare", "hm_attn_with_kv",
     "hm_causal_conv1d", "hm_selective_scan", "hm_selective_scan_workspace",
-    "hm_conv_selective_scan", "hm_branch_norm_mean",
+    "hm_conv_selective_scan", "hm_branch_norm_mean", "hm_linear_bf16",
     "hm_mixer_prefill", "hm_mixer_prefill_workspace",
     "hm_mixer_step", "hm_mixer_step_workspace",
     "hm_debug_attn_mask", "hm_debug_tile_plan", "hm_debug_attn_tiles", "hm_debug_cache_slot",
@@ -95,6 +95,8 @@ def _load():
     lib.hm_selective_scan_workspace.restype = _sz
     lib.hm_conv_selective_scan.argtypes = [_vp] * 14 + [_i] * 6 + [_vp, _sz, _vp]
     lib.hm_branch_norm_mean.argtypes = [_vp, _vp, _vp, _vp, _f, _vp, _ll, _i, _i, _vp]
+    lib.hm_linear_bf16.argtypes = [_vp, _vp, _i, _i, _i, _i, ctypes.POINTER(_vp),
+                                   ctypes.POINTER(_i), _vp]
     lib.hm_mixer_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
     lib.hm_mixer_prefill_workspace.argtypes = [ctypes.POINTER(PrefillArgs)]
     lib.hm_mixer_prefill_workspace.restype = _sz

@@ -15,7 +15,7 @@ from . import HM_BF16, HM_F32, HmError, PrefillArgs, StepArgs, lib
 
 __all__ = [
     "swa_meta_attn", "attn_kv_bytes", "attn_kv_prepare", "attn_with_kv", "causal_conv1d", "selective_scan", "conv_selective_scan",
-    "branch_norm_mean", "mixer_prefill", "PrefillPlan", "mixer_step", "StepPlan",
+    "branch_norm_mean", "linear", "mixer_prefill", "PrefillPlan", "mixer_step", "StepPlan",
     "debug_attn_mask", "debug_tile_plan", "debug_attn_tiles", "debug_cache_slot",
     "dtype_code",
 ]
@@ -173,6 +173,27 @@ def branch_norm_mean(ya, ys, beta_a, beta_s, eps: float = 1e-6, out=None):
     _check(lib.hm_branch_norm_mean(_p(ya), _p(ys), _p(beta_a), _p(beta_s), eps, _p(out), rows,
                                    width, dtype_code(ya), _stream()))
     return out
+
+
+# ------------------------------------------------------------------ projections
+def linear(x, w, seg_cols=None, outs=None):
+    """y = x w^T (bf16; w in nn.Linear layout [N, K]) over the last dim of x.
+    seg_cols splits the N output columns into tensors of those widths (a list
+    is returned); default: one tensor [..., N]."""
+    _dev(x, w)
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("linear takes bf16 x and w")
+    K = x.shape[-1]
+    M = x.numel() // K
+    N = w.shape[0]
+    cols = [N] if seg_cols is None else list(seg_cols)
+    if outs is None:
+        outs = [torch.empty(x.shape[:-1] + (c,), dtype=x.dtype, device=x.device) for c in cols]
+    _dev(*outs)
+    ptrs = (ctypes.c_void_p * len(cols))(*[o.data_ptr() for o in outs])
+    widths = (ctypes.c_int * len(cols))(*cols)
+    _check(lib.hm_linear_bf16(_p(x), _p(w), M, N, K, len(cols), ptrs, widths, _stream()))
+    return outs if seg_cols is not None else outs[0]
 
 
 # ------------------------------------------------------------------ whole layer

@@ -159,6 +159,21 @@ hm_status hm_branch_norm_mean(const void* ya, const void* ys, const float* beta_
                               long long rows, int width, hm_dtype dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Projections around the mixer (Hymba blog, 数学表示 §2: X~ times W_in_proj
+ * gives Q, K, V, the SSM input and the gate G; §5: W_out_proj maps the fused
+ * output back to the model width).
+ *   y = x W^T: x [M, K] bf16, w [N, K] bf16 (nn.Linear layout), float32
+ *   accumulation, results rounded to bf16.
+ * The N output columns are split into n_seg consecutive segments: segment s
+ * has seg_cols[s] columns (a positive multiple of 32) and is written to
+ * outs[s] as [M, seg_cols[s]], so an in-projection writes Q, K, V, x and z
+ * into their own tensors.  outs and seg_cols are HOST arrays of n_seg
+ * entries (1 <= n_seg <= 8; widths summing to N).  K must be a multiple of 64.
+ * ---------------------------------------------------------------------- */
+hm_status hm_linear_bf16(const void* x, const void* w, int M, int N, int K, int n_seg,
+                         void* const* outs, const int* seg_cols, void* stream);
+
+/* ------------------------------------------------------------------------
  * One whole mixer layer in prefill: attention and the SSM branch
  * (hm_conv_selective_scan from zero states) on the same X~, then
  * hm_branch_norm_mean.  Width Di must equal Hq * Dh.

@@ -32,10 +32,11 @@ from .scan import selective_scan, scan_step
 from .norm import rms_normalize, branch_norm_mean
 from .mixer import mixer_prefill, meta_cache, mixer_prefill_cached_meta
 from .step import build_cache, valid_slots, mixer_step, mixer_step_ragged
+from .linear import linear, split_columns
 
 __all__ = [
     "visible", "mask", "mask_rows", "visible_count", "tile_kinds", "cache_slot",
     "rope_angles", "rope", "rope_at", "attention", "causal_conv1d", "conv_step",
     "selective_scan", "scan_step", "rms_normalize", "branch_norm_mean",
-    "mixer_prefill", "meta_cache", "mixer_prefill_cached_meta", "build_cache", "valid_slots", "mixer_step", "mixer_step_ragged",
+    "mixer_prefill", "meta_cache", "mixer_prefill_cached_meta", "build_cache", "valid_slots", "mixer_step", "mixer_step_ragged", "linear", "split_columns",
 ]

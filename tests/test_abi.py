@@ -205,3 +205,18 @@ def test_empty_extents_are_rejected():
     s = hm.StepArgs(B=0, Hq=2, Hkv=1, Dh=16, Di=32, N=16, K=4, n_meta=4, window=16,
                     cache_slots=16, n_prev=3, rope_base=1e4, eps=1e-6, dtype=hm.HM_F32)
     assert L.hm_mixer_step(ctypes.byref(s), None) == hm.HM_ERR_INVALID
+
+
+def test_linear_rejects_bad_arguments():
+    L = hm.lib
+    outs = (ctypes.c_void_p * 2)(3 << 20, 4 << 20)
+    widths = (ctypes.c_int * 2)(32, 64)
+    x, w = ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20)
+    assert L.hm_linear_bf16(x, w, 8, 96, 100, 2, outs, widths, None) == hm.HM_ERR_UNSUPPORTED
+    assert L.hm_linear_bf16(x, w, 8, 95, 64, 2, outs, widths, None) == hm.HM_ERR_INVALID
+    bad = (ctypes.c_int * 2)(48, 48)                  # not multiples of 32
+    assert L.hm_linear_bf16(x, w, 8, 96, 64, 2, outs, bad, None) == hm.HM_ERR_INVALID
+    assert L.hm_linear_bf16(x, w, 0, 96, 64, 2, outs, widths, None) == hm.HM_ERR_INVALID
+    assert L.hm_linear_bf16(x, w, 8, 96, 64, 9, outs, widths, None) == hm.HM_ERR_INVALID
+    alias = (ctypes.c_void_p * 2)(1 << 20, 4 << 20)   # output aliases x
+    assert L.hm_linear_bf16(x, w, 8, 96, 64, 2, alias, widths, None) == hm.HM_ERR_INVALID
