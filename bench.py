@@ -21,6 +21,7 @@ Also reported on the same JSON line:
                 32-layer stack (batch 2, 128 + 16384 tokens, layers 0/15/31
                 global, adjacent sliding-window layers sharing prepared K/V);
   ragged_decode the decode pair with one n_prev per sequence (warm);
+  projections   the in- and out-projections around the layer (bf16 MFMA GEMM);
   cached_meta   the same layer with the meta tokens' K/V and SSM states taken
                 from a cache: only the 2048 real-token rows are computed
                 (real tokens/s, beside the full layer's real tokens/s);
@@ -338,6 +339,24 @@ def main():
     ms_cached = timed(cplan.run, args.steps, args.warmup)
     del cplan, ct, cmk
 
+    # the projections around the layer: in-projection of the 2176 rows from width
+    # 1600 into Q, K, V, x, z (5440 columns) and the out-projection (1600 -> 1600)
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    d_model = shape.Hq * shape.Dh
+    segs = [shape.Hq * shape.Dh, shape.Hkv * shape.Dh, shape.Hkv * shape.Dh, shape.Di, shape.Di]
+    px = torch.randn(shape.B * shape.T, d_model, device="cuda", generator=gen).bfloat16()
+    pw_in = (torch.randn(sum(segs), d_model, device="cuda", generator=gen)
+             / d_model ** 0.5).bfloat16()
+    pw_out = (torch.randn(d_model, shape.Di, device="cuda", generator=gen)
+              / shape.Di ** 0.5).bfloat16()
+    pouts = [torch.empty(shape.B * shape.T, c, dtype=torch.bfloat16, device="cuda") for c in segs]
+    py = torch.empty(shape.B * shape.T, d_model, dtype=torch.bfloat16, device="cuda")
+    ms_in = timed(lambda: hm.linear(px, pw_in, seg_cols=segs, outs=pouts), args.steps, args.warmup)
+    ms_out = timed(lambda: hm.linear(pouts[3], pw_out, outs=[py]), args.steps, args.warmup)
+    fl_in = 2.0 * shape.B * shape.T * sum(segs) * d_model
+    fl_out = 2.0 * shape.B * shape.T * d_model * shape.Di
+    del px, pw_in, pw_out, pouts, py
+
     # dominant kernel on its own: attention over the prepared K/V
     ms_attn = timed(lambda: hm.attn_with_kv(t["q"], plan.kv, shape.Hkv, shape.M, shape.W,
                                             shape.rope_base, out=plan.ya),
@@ -432,6 +451,15 @@ def main():
                         "real_tokens_per_s": shape.B * shape.N / (ms_cached * 1e-3),
                         "ms_per_layer": ms_cached,
                         "full_layer_real_tokens_per_s": shape.B * shape.N / (ms * 1e-3)},
+        "projections": {
+            "workload": shape.name + " in-projection 1600 -> Q, K, V, x, z (5440) and "
+                                     "out-projection 1600 -> 1600, bf16",
+            "in_proj": {"ms": ms_in, "achieved": fl_in / (ms_in * 1e-3) / 1e12,
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": fl_in / (ms_in * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+            "out_proj": {"ms": ms_out, "achieved": fl_out / (ms_out * 1e-3) / 1e12,
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": fl_out / (ms_out * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}},
         "layer_step_us": layer_dist,
         "sclk_mhz": sclk,
         "breakdown_ms": {"layer_one_stream": ms, "layer_two_streams": ms_two,
