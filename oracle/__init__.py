@@ -14,7 +14,9 @@ pages' description of the method:
 * branch normalisation and averaging — Hymba blog, "深入理解混合头模块" and
   "数学表示" §5; Telegram post "Mamba, Jamba, Ху...Hymba!" (outputs averaged);
 * GQA and RoPE — Hymba-1.5B-Base model card, "模型架构" (model architecture);
-* cross-layer KV sharing — Hymba blog, "Hymba 的整体架构".
+* cross-layer KV sharing — Hymba blog, "Hymba 的整体架构";
+* whole blocks (norm, mixer, norm, FFN) and their stack — Hymba blog,
+  "Hymba 的整体架构" and "数学表示" §2, §5; model card, "模型架构".
 
 Readings of silent or garbled points (softmax scale, window off-by-one, RoPE
 variant, conv, D term, SiLU gate, RMS norm, epsilon, sum vs average) are stated
@@ -33,10 +35,12 @@ from .norm import rms_normalize, branch_norm_mean
 from .mixer import mixer_prefill, meta_cache, mixer_prefill_cached_meta
 from .step import build_cache, valid_slots, mixer_step, mixer_step_ragged
 from .linear import linear, split_columns
+from .block import rms_norm, silu, softplus, ffn, block_prefill, stack_prefill
 
 __all__ = [
     "visible", "mask", "mask_rows", "visible_count", "tile_kinds", "cache_slot",
     "rope_angles", "rope", "rope_at", "attention", "causal_conv1d", "conv_step",
     "selective_scan", "scan_step", "rms_normalize", "branch_norm_mean",
     "mixer_prefill", "meta_cache", "mixer_prefill_cached_meta", "build_cache", "valid_slots", "mixer_step", "mixer_step_ragged", "linear", "split_columns",
+    "rms_norm", "silu", "softplus", "ffn", "block_prefill", "stack_prefill",
 ]

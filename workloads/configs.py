@@ -38,6 +38,9 @@ class MixerShape:
     # stack-only
     layers: int = 1
     global_layers: Tuple[int, ...] = field(default_factory=tuple)
+    # whole blocks only: model width (the in-projection's input) and FFN width
+    d_model: int = 0
+    d_ffn: int = 0
 
     @property
     def T(self) -> int:
@@ -54,6 +57,10 @@ DECODE_PAIR = MixerShape("decode-pair-b64-cache1152", B=64, M=128, N=1, Hq=25, H
                          Dh=64, W=1024, Di=1600, n_prev=2048, cache_slots=1024)
 STACK = MixerShape("stack32-b2-t16512", B=2, M=128, N=16384, Hq=25, Hkv=5, Dh=64,
                    W=1024, Di=1600, layers=32, global_layers=(0, 15, 31))
+
+# Whole blocks (norm, mixer, norm, FFN) at the model card's widths 1600 / 5504.
+BLOCK_SWA = replace(SWA_PREFILL, name="block-swa-prefill-b1-t2176", d_model=1600, d_ffn=5504)
+BLOCK_STACK = replace(STACK, name="block-stack32-b2-t16512", d_model=1600, d_ffn=5504)
 
 ALL = (TINY, SWA_PREFILL, GLOBAL_PREFILL, DECODE_PAIR, STACK)
 

@@ -135,6 +135,84 @@ def decode_inputs(shape: MixerShape, seed=0) -> dict:
     return out
 
 
+def block_weight_rows(shape: MixerShape, producer: bool) -> int:
+    """Rows of a block's in-projection: Q, [K, V,] x, z."""
+    return shape.Hq * shape.Dh + (2 * shape.Hkv * shape.Dh if producer else 0) + 2 * shape.Di
+
+
+def block_inputs(shape: MixerShape, seed=0, layer: int = 0, producer: bool = True) -> dict:
+    """Hidden states and weights of one whole block (model width d = d_model,
+    FFN width F = d_ffn).  Distributions:
+
+      hidden ~ N(0, 1) [B, T, d]
+      ln1, ln2 ~ 1 + 0.1 N(0, 1) [d]
+      w_in ~ N(0, 1) / sqrt(d)    [block_weight_rows, d]
+      w_dbc: the first Di rows 0.5 N(0, 1) / sqrt(Di), the last 2 Ns rows
+             N(0, 1) / sqrt(Di)   [Di + 2 Ns, Di]
+      dt_bias ~ -2 + 0.1 N(0, 1) [Di]
+      A, D, conv_w, conv_b, beta_a, beta_s as for the mixer core
+      w_out ~ N(0, 1) / sqrt(Di) [d, Di]; w_up ~ N(0, 1) / sqrt(d) [F, d];
+      w_down ~ N(0, 1) / sqrt(F) [d, F]
+
+    Draw order: hidden, ln1, w_in, w_dbc, dt_bias, the mixer parameters, w_out,
+    ln2, w_up, w_down; seed sequence [seed, layer].  Matrices and hidden states
+    are activations (bf16-rounded for bf16 workloads); vectors are float32.
+    """
+    rng = np.random.default_rng([seed, layer])
+    B, T, dt = shape.B, shape.T, shape.dtype
+    d, F, Di, Ns = shape.d_model, shape.d_ffn, shape.Di, shape.Ns
+    out = {"hidden": _act(rng.standard_normal((B, T, d)), dt)}
+    out["ln1"] = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    out["w_in"] = _act(rng.standard_normal((block_weight_rows(shape, producer), d)) / np.sqrt(d), dt)
+    wd = rng.standard_normal((Di + 2 * Ns, Di)) / np.sqrt(Di)
+    wd[:Di] *= 0.5
+    out["w_dbc"] = _act(wd, dt)
+    out["dt_bias"] = (-2.0 + 0.1 * rng.standard_normal(Di)).astype(np.float32)
+    out.update(_params(rng, Di, Ns, shape.K))
+    out["w_out"] = _act(rng.standard_normal((d, Di)) / np.sqrt(Di), dt)
+    out["ln2"] = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    out["w_up"] = _act(rng.standard_normal((F, d)) / np.sqrt(d), dt)
+    out["w_down"] = _act(rng.standard_normal((d, F)) / np.sqrt(F), dt)
+    return out
+
+
+def block_inputs_torch(shape: MixerShape, seed: int, layer: int, producer: bool, device,
+                       hidden: bool = False) -> dict:
+    """Device-side generator of one block's weights (and, with ``hidden``, its
+    input hidden states) for the large stack workload: the distributions of
+    ``block_inputs``, torch's Philox stream instead of PCG64."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1_000_003 + 7919 * int(layer) + 17)
+    act = torch.bfloat16 if shape.dtype == "bf16" else torch.float32
+    d, F, Di, Ns, K = shape.d_model, shape.d_ffn, shape.Di, shape.Ns, shape.K
+
+    def n(*s):
+        return torch.randn(*s, generator=g, device=device, dtype=torch.float32)
+
+    out = {}
+    if hidden:
+        out["hidden"] = n(shape.B, shape.T, d).to(act)
+    out["ln1"] = 1.0 + 0.1 * n(d)
+    out["w_in"] = (n(block_weight_rows(shape, producer), d) / float(np.sqrt(d))).to(act)
+    wd = n(Di + 2 * Ns, Di) / float(np.sqrt(Di))
+    wd[:Di] *= 0.5
+    out["w_dbc"] = wd.to(act)
+    out["dt_bias"] = -2.0 + 0.1 * n(Di)
+    out["A"] = -torch.exp(n(Di, Ns) * 0.5)
+    out["D"] = n(Di)
+    out["conv_w"] = n(Di, K) / float(np.sqrt(K))
+    out["conv_b"] = 0.1 * n(Di)
+    out["beta_a"] = 1.0 + 0.1 * n(Di)
+    out["beta_s"] = 1.0 + 0.1 * n(Di)
+    out["w_out"] = (n(d, Di) / float(np.sqrt(Di))).to(act)
+    out["ln2"] = 1.0 + 0.1 * n(d)
+    out["w_up"] = (n(F, d) / float(np.sqrt(d))).to(act)
+    out["w_down"] = (n(d, F) / float(np.sqrt(F))).to(act)
+    return out
+
+
 def prefill_inputs_torch(shape: MixerShape, seed: int, layer: int, device):
     """Device-side generator for the large stack workload (same distributions,
     torch's Philox stream instead of PCG64; activations rounded to bf16).
@@ -171,7 +249,8 @@ def prefill_inputs_torch(shape: MixerShape, seed: int, layer: int, device):
     return out
 
 
-ACT_KEYS = ("q", "k", "v", "x", "delta", "Bm", "Cm", "z", "k_new", "v_new", "k_cache", "v_cache")
+ACT_KEYS = ("q", "k", "v", "x", "delta", "Bm", "Cm", "z", "k_new", "v_new", "k_cache", "v_cache",
+            "hidden", "w_in", "w_dbc", "w_out", "w_up", "w_down")
 
 
 def to_device(d: dict, dtype: str, device="cuda") -> dict:
