@@ -21,14 +21,16 @@ LIB_PATH = os.path.join(HERE, "libhm.so")
 
 HM_OK, HM_ERR_INVALID, HM_ERR_UNSUPPORTED, HM_ERR_WORKSPACE, HM_ERR_HIP = range(5)
 HM_F32, HM_BF16 = 0, 1
+HM_ACT_NONE, HM_ACT_SILU, HM_ACT_SOFTPLUS = 0, 1, 2
 
 EXPORTS = (
     "hm_abi_version", "hm_status_string", "hm_last_error",
     "hm_swa_meta_attn", "hm_swa_meta_attn_workspace",
     "hm_attn_kv_bytes", "hm_attn_kv_prepare", "hm_attn_with_kv",
     "hm_causal_conv1d", "hm_selective_scan", "hm_selective_scan_workspace",
-    "hm_conv_selective_scan", "hm_branch_norm_mean", "hm_linear_bf16",
-    "hm_mixer_prefill", "hm_mixer_prefill_workspace",
+    "hm_conv_selective_scan", "hm_branch_norm_mean", "hm_linear_bf16", "hm_linear_bf16_ex",
+    "hm_rms_norm", "hm_mixer_prefill", "hm_mixer_prefill_workspace",
+    "hm_block_prefill", "hm_block_prefill_workspace",
     "hm_mixer_step", "hm_mixer_step_workspace",
     "hm_debug_attn_mask", "hm_debug_tile_plan", "hm_debug_attn_tiles", "hm_debug_cache_slot",
 )
@@ -68,6 +70,20 @@ class StepArgs(ctypes.Structure):
         ("workspace_bytes", _sz), ("n_prev_seq", _vp)]
 
 
+class LinearEpilogue(ctypes.Structure):
+    _fields_ = [("bias", _vp), ("residual", _vp), ("act", _i)]
+
+
+class BlockArgs(ctypes.Structure):
+    _fields_ = [(n, _i) for n in ("B", "T", "d_model", "d_ffn", "Hq", "Hkv", "Dh", "Di", "N", "K",
+                                  "n_meta", "window")] + [
+        ("pos0", _ll), ("rope_base", _f), ("scale", _f), ("eps", _f), ("dtype", _i),
+    ] + [(n, _vp) for n in ("hidden", "ln1", "ln2", "w_in", "w_dbc", "dt_bias", "A", "D",
+                            "conv_w", "conv_b", "beta_a", "beta_s", "w_out", "w_up", "w_down",
+                            "kv")] + [("kv_bytes", _sz), ("kv_reuse", _i), ("workspace", _vp),
+                                      ("workspace_bytes", _sz)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: run `python hybrid_head_lm_amd/build.py` "
@@ -97,6 +113,12 @@ def _load():
     lib.hm_branch_norm_mean.argtypes = [_vp, _vp, _vp, _vp, _f, _vp, _ll, _i, _i, _vp]
     lib.hm_linear_bf16.argtypes = [_vp, _vp, _i, _i, _i, _i, ctypes.POINTER(_vp),
                                    ctypes.POINTER(_i), _vp]
+    lib.hm_linear_bf16_ex.argtypes = [_vp, _vp, _i, _i, _i, _i, ctypes.POINTER(_vp),
+                                      ctypes.POINTER(_i), ctypes.POINTER(LinearEpilogue), _vp]
+    lib.hm_rms_norm.argtypes = [_vp, _vp, _f, _vp, _ll, _i, _i, _vp]
+    lib.hm_block_prefill.argtypes = [ctypes.POINTER(BlockArgs), _vp]
+    lib.hm_block_prefill_workspace.argtypes = [ctypes.POINTER(BlockArgs)]
+    lib.hm_block_prefill_workspace.restype = _sz
     lib.hm_mixer_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _vp]
     lib.hm_mixer_prefill_workspace.argtypes = [ctypes.POINTER(PrefillArgs)]
     lib.hm_mixer_prefill_workspace.restype = _sz
@@ -117,4 +139,4 @@ if lib.hm_abi_version() != 1:
     raise ImportError("libhm ABI version mismatch")
 
 from .api import *  # noqa: E402,F401,F403
-from .stack import StackPlan  # noqa: E402,F401
+from .stack import BlockStack, StackPlan  # noqa: E402,F401

@@ -11,11 +11,12 @@ import ctypes
 
 import torch
 
-from . import HM_BF16, HM_F32, HmError, PrefillArgs, StepArgs, lib
+from . import (HM_ACT_NONE, HM_ACT_SILU, HM_ACT_SOFTPLUS, HM_BF16, HM_F32, BlockArgs, HmError,
+               LinearEpilogue, PrefillArgs, StepArgs, lib)
 
 __all__ = [
     "swa_meta_attn", "attn_kv_bytes", "attn_kv_prepare", "attn_with_kv", "causal_conv1d", "selective_scan", "conv_selective_scan",
-    "branch_norm_mean", "linear", "mixer_prefill", "PrefillPlan", "mixer_step", "StepPlan",
+    "branch_norm_mean", "linear", "rms_norm", "BlockPlan", "mixer_prefill", "PrefillPlan", "mixer_step", "StepPlan",
     "debug_attn_mask", "debug_tile_plan", "debug_attn_tiles", "debug_cache_slot",
     "dtype_code",
 ]
@@ -176,10 +177,16 @@ def branch_norm_mean(ya, ys, beta_a, beta_s, eps: float = 1e-6, out=None):
 
 
 # ------------------------------------------------------------------ projections
-def linear(x, w, seg_cols=None, outs=None):
+_ACTS = {None: HM_ACT_NONE, "silu": HM_ACT_SILU, "softplus": HM_ACT_SOFTPLUS}
+
+
+def linear(x, w, seg_cols=None, outs=None, epilogues=None):
     """y = x w^T (bf16; w in nn.Linear layout [N, K]) over the last dim of x.
     seg_cols splits the N output columns into tensors of those widths (a list
-    is returned); default: one tensor [..., N]."""
+    is returned); default: one tensor [..., N].  epilogues: one dict per
+    segment with optional "bias" (f32 [width]), "act" (None, "silu",
+    "softplus") and "residual" (bf16 [..., width]; may be the output itself):
+    y = act(x w^T + bias) + residual."""
     _dev(x, w)
     if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
         raise TypeError("linear takes bf16 x and w")
@@ -192,8 +199,90 @@ def linear(x, w, seg_cols=None, outs=None):
     _dev(*outs)
     ptrs = (ctypes.c_void_p * len(cols))(*[o.data_ptr() for o in outs])
     widths = (ctypes.c_int * len(cols))(*cols)
-    _check(lib.hm_linear_bf16(_p(x), _p(w), M, N, K, len(cols), ptrs, widths, _stream()))
+    if epilogues is None:
+        _check(lib.hm_linear_bf16(_p(x), _p(w), M, N, K, len(cols), ptrs, widths, _stream()))
+    else:
+        if len(epilogues) != len(cols):
+            raise ValueError("one epilogue per segment")
+        eps = (LinearEpilogue * len(cols))()
+        for e, d in zip(eps, epilogues):
+            d = d or {}
+            bias, res = d.get("bias"), d.get("residual")
+            _dev(bias, res)
+            _f32(bias)
+            if d.get("act") not in _ACTS:
+                raise ValueError(f"unknown activation {d.get('act')!r}")
+            e.bias = None if bias is None else bias.data_ptr()
+            e.residual = None if res is None else res.data_ptr()
+            e.act = _ACTS[d.get("act")]
+        _check(lib.hm_linear_bf16_ex(_p(x), _p(w), M, N, K, len(cols), ptrs, widths, eps,
+                                     _stream()))
     return outs if seg_cols is not None else outs[0]
+
+
+def rms_norm(x, w, eps: float = 1e-6, out=None):
+    """x / sqrt(mean(x^2) + eps) * w over the last dim (w float32)."""
+    _dev(x, w)
+    _f32(w)
+    out = torch.empty_like(x) if out is None else out
+    _dev(out)
+    width = x.shape[-1]
+    _check(lib.hm_rms_norm(_p(x), _p(w), eps, _p(out), x.numel() // width, width, dtype_code(x),
+                           _stream()))
+    return out
+
+
+class BlockPlan:
+    """One whole Hymba block (norm, in-projection, mixer, out-projection, norm,
+    FFN) over ``hidden`` [B, T, d_model] (bf16, updated in place by ``run()``).
+
+    ``w`` maps ln1, ln2, w_in, w_dbc, dt_bias, A, D, conv_w, conv_b, beta_a,
+    beta_s, w_out, w_up, w_down to device tensors (matrices bf16 in nn.Linear
+    layout, vectors float32).  kv: prepared K/V buffer (allocated when None);
+    kv_reuse: attend over kv as an earlier block prepared it (w_in then has
+    rows Q, x, z only).  ``run()`` allocates nothing."""
+
+    def __init__(self, w: dict, hidden, Hq: int, Hkv: int, n_meta: int, window: int,
+                 rope_base: float = 10000.0, eps: float = 1e-6, pos0: int = 0, scale: float = 0.0,
+                 kv=None, kv_reuse=False, workspace=None):
+        keys = ("ln1", "ln2", "w_in", "w_dbc", "dt_bias", "A", "D", "conv_w", "conv_b",
+                "beta_a", "beta_s", "w_out", "w_up", "w_down")
+        dev = _dev(hidden, *[w[k] for k in keys])
+        _f32(*[w[k] for k in ("ln1", "ln2", "dt_bias", "A", "D", "conv_w", "conv_b", "beta_a",
+                              "beta_s")])
+        B, T, d_model = hidden.shape
+        Di, N = w["A"].shape
+        Dh = Di // Hq
+        a = BlockArgs()
+        a.B, a.T, a.d_model, a.d_ffn = B, T, d_model, w["w_up"].shape[0]
+        a.Hq, a.Hkv, a.Dh, a.Di, a.N, a.K = Hq, Hkv, Dh, Di, N, w["conv_w"].shape[1]
+        a.n_meta, a.window, a.pos0 = n_meta, window, pos0
+        a.rope_base, a.scale, a.eps, a.dtype = rope_base, scale, eps, dtype_code(hidden)
+        a.hidden = hidden.data_ptr()
+        for k in keys:
+            setattr(a, k, w[k].data_ptr())
+        if kv is None:
+            if kv_reuse:
+                raise ValueError("kv_reuse needs the producer's kv buffer")
+            kv = _ws(lib.hm_attn_kv_bytes(B, T, Hkv, Dh, dtype_code(hidden)), dev)
+        self.kv = kv
+        a.kv, a.kv_bytes, a.kv_reuse = kv.data_ptr(), kv.numel() * kv.element_size(), int(kv_reuse)
+        nb = lib.hm_block_prefill_workspace(ctypes.byref(a))
+        self.ws = workspace if workspace is not None else _ws(nb, dev)
+        a.workspace, a.workspace_bytes = self.ws.data_ptr(), self.ws.numel()
+        self.args, self.w, self.hidden = a, w, hidden
+
+    @staticmethod
+    def workspace_bytes(**kw) -> int:
+        a = BlockArgs()
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return lib.hm_block_prefill_workspace(ctypes.byref(a))
+
+    def run(self, stream=None):
+        s = _stream() if stream is None else ctypes.c_void_p(stream.cuda_stream)
+        _check(lib.hm_block_prefill(ctypes.byref(self.args), s))
+        return self.hidden
 
 
 # ------------------------------------------------------------------ whole layer

@@ -81,7 +81,12 @@ size_t hm_mixer_prefill_workspace(const hm_prefill_args* a) {
   return ws;
 }
 
-hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream) {
+}  // extern "C"
+
+namespace hm {
+
+// dry_only: validate every part and launch nothing.
+hm_status mixer_prefill_impl(const hm_prefill_args* a, hipStream_t stream, bool dry_only) {
   HM_REQUIRE(a != nullptr, HM_ERR_INVALID, "args is NULL");
   HM_REQUIRE(a->Di == a->Hq * a->Dh, HM_ERR_INVALID, "Di must equal Hq * Dh");
   HM_PTR(a->ya);
@@ -107,13 +112,13 @@ hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream) {
   char* ws = (char*)a->workspace;
   void* kv = a->kv ? a->kv : (void*)(ws + wscan);
   const size_t kvb = a->kv ? a->kv_bytes : a->workspace_bytes - wscan;
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = stream;
   hipStream_t st2 = a->stream2 ? (hipStream_t)a->stream2 : st;
   HM_REQUIRE(st2 != st || a->stream2 == nullptr, HM_ERR_INVALID, "stream2 must differ from stream");
   // Validate all parts before the first launch, so that a failure leaves
   // every output untouched.  bf16 layers on one stream then run the fused
   // launch sequence; the others run the parts one by one.
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < (dry_only ? 1 : 2); ++pass) {
     const bool dry = pass == 0;
     hm_status s;
     if (!dry && hm::prefill_fusable(a)) return hm::prefill_fused_bf16(a, kv, ws, st);
@@ -145,6 +150,14 @@ hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream) {
     if (s != HM_OK) return s;
   }
   return HM_OK;
+}
+
+}  // namespace hm
+
+extern "C" {
+
+hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream) {
+  return hm::mixer_prefill_impl(a, (hipStream_t)stream, false);
 }
 
 long long hm_debug_cache_slot(long long n_prev, int n_meta, int window) {

@@ -155,6 +155,12 @@ hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, 
 hm_status norm_mean_impl(const void* ya, const void* ys, const float* beta_a,
                          const float* beta_s, float eps, void* out, long long rows,
                          int width, hm_dtype dtype, hipStream_t st, bool dry);
+hm_status rms_norm_impl(const void* x, const float* w, float eps, void* out, long long rows,
+                        int width, hm_dtype dtype, hipStream_t st, bool dry);
+hm_status linear_launch(const void* x, const void* w, int M, int N, int K, int n_seg,
+                        void* const* outs, const int* seg_cols, const hm_linear_epilogue* ep,
+                        hipStream_t st, bool dry = false);
+hm_status mixer_prefill_impl(const hm_prefill_args* a, hipStream_t st, bool dry_only);
 
 }  // namespace hm
 

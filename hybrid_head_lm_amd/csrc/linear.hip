@@ -10,8 +10,11 @@
 // 16-byte chunk c of row r in slot c ^ ((r >> 1) & 7): the 16 lanes of an
 // operand read take one chunk of 16 consecutive rows from 16 different bank
 // groups.  The output columns may be split into segments written to separate
-// tensors (the in-projection's Q, K, V, x and z).
+// tensors (the in-projection's Q, K, V, x and z), each with its own epilogue:
+// a bias, an activation (SiLU for the FFN's hidden layer, softplus for the
+// SSM step sizes) and a residual added last (the block's skip connections).
 #include <algorithm>
+#include <cmath>
 
 #include "hm_common.h"
 
@@ -21,10 +24,20 @@ constexpr int kGM = 128, kGN = 128, kGK = 64;   // workgroup tile (rows, columns
 constexpr int kMaxSeg = 8;
 
 struct LinOut {
-  bf16_t* p[kMaxSeg];        // segment outputs, [M, col0[s+1] - col0[s]]
-  int col0[kMaxSeg + 1];     // segment s holds the output columns [col0[s], col0[s+1])
-  int n;                     // segments
+  bf16_t* p[kMaxSeg];          // segment outputs, [M, col0[s+1] - col0[s]]
+  const float* bias[kMaxSeg];  // per segment: [width] f32 or null
+  const bf16_t* res[kMaxSeg];  // per segment: [M, width] or null (may be p[s] itself)
+  int act[kMaxSeg];            // per segment: HM_ACT_*
+  int col0[kMaxSeg + 1];       // segment s holds the output columns [col0[s], col0[s+1])
+  int n;                       // segments
 };
+
+// v + bias, then the activation, then + residual, in float32.
+HM_DEV float lin_act(float v, int act) {
+  if (act == HM_ACT_SILU) return v / (1.f + __expf(-v));
+  if (act == HM_ACT_SOFTPLUS) return v > 20.f ? v : log1pf(__expf(v));
+  return v;
+}
 
 HM_DEV int lin_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
 HM_DEV int lin_off(int row, int c) { return row * 128 + (lin_slot(row, c) << 4); }
@@ -101,33 +114,45 @@ __global__ __launch_bounds__(256) void linear_bf16(const bf16_t* __restrict__ x,
   }
 
   // Output: element r of block (i, j) is row 32 i + 8 (r / 4) + 4 hk + r % 4 and
-  // column 32 j + lane % 32 of the quarter.  A 32-column block lies in one
-  // segment (segment widths are multiples of 32).
+  // column 32 j + lane % 32 of the quarter.  Each lane finds the segment of
+  // its own column (segment widths are multiples of 16, so a 32-column block
+  // may straddle two).  A residual that is the output itself is read and
+  // written by the same lane.
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int nb = n0 + 64 * wc + 32 * j;
-    if (nb >= N) continue;
+    const int col = n0 + 64 * wc + 32 * j + r32;
+    if (col >= N) continue;
     int s = 0;
-    while (s + 1 < out.n && nb >= out.col0[s + 1]) ++s;
+    while (s + 1 < out.n && col >= out.col0[s + 1]) ++s;
     bf16_t* dst = out.p[s];
+    const bf16_t* res = out.res[s];
+    const int act = out.act[s];
     const int ld = out.col0[s + 1] - out.col0[s];
-    const int cn = nb - out.col0[s] + r32;
+    const int cn = col - out.col0[s];
+    const float bv = out.bias[s] ? out.bias[s][cn] : 0.f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + 64 * wr + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
-        if (row < M) dst[(size_t)row * ld + cn] = f2bf(acc[i][j][r]);
+        if (row < M) {
+          const size_t e = (size_t)row * ld + cn;
+          float v = lin_act(acc[i][j][r] + bv, act);
+          if (res) v += bf2f(res[e]);
+          dst[e] = f2bf(v);
+        }
       }
   }
 }
 
 }  // namespace
 
-extern "C" {
+namespace hm {
 
-hm_status hm_linear_bf16(const void* x, const void* w, int M, int N, int K, int n_seg,
-                         void* const* outs, const int* seg_cols, void* stream) {
+// Validates the arguments, then one launch.
+hm_status linear_launch(const void* x, const void* w, int M, int N, int K, int n_seg,
+                        void* const* outs, const int* seg_cols, const hm_linear_epilogue* ep,
+                        hipStream_t st, bool dry) {
   HM_PTR(x);
   HM_PTR(w);
   HM_REQUIRE(M > 0 && N > 0 && K > 0, HM_ERR_INVALID, "M, N and K must be positive");
@@ -141,18 +166,49 @@ hm_status hm_linear_bf16(const void* x, const void* w, int M, int N, int K, int 
   o.n = n_seg;
   o.col0[0] = 0;
   for (int s = 0; s < n_seg; ++s) {
-    HM_REQUIRE(seg_cols[s] > 0 && seg_cols[s] % 32 == 0, HM_ERR_INVALID,
-               "segment widths must be positive multiples of 32");
+    HM_REQUIRE(seg_cols[s] > 0 && seg_cols[s] % 16 == 0, HM_ERR_INVALID,
+               "segment widths must be positive multiples of 16");
     HM_PTR(outs[s]);
     HM_REQUIRE(outs[s] != x && outs[s] != w, HM_ERR_INVALID, "outputs must not alias x or w");
+    for (int t = 0; t < s; ++t)
+      HM_REQUIRE(outs[t] != outs[s], HM_ERR_INVALID, "segment outputs must be distinct");
     o.p[s] = (bf16_t*)outs[s];
     o.col0[s + 1] = o.col0[s] + seg_cols[s];
+    if (ep) {
+      HM_REQUIRE(ep[s].act == HM_ACT_NONE || ep[s].act == HM_ACT_SILU ||
+                     ep[s].act == HM_ACT_SOFTPLUS,
+                 HM_ERR_INVALID, "unknown activation");
+      HM_REQUIRE(ep[s].residual == nullptr || (ep[s].residual != x && ep[s].residual != w),
+                 HM_ERR_INVALID, "a residual must not alias x or w");
+      for (int t = 0; t < n_seg; ++t)
+        HM_REQUIRE(ep[s].residual == nullptr || t == s || ep[s].residual != outs[t],
+                   HM_ERR_INVALID, "a residual may only alias its own segment's output");
+      o.bias[s] = ep[s].bias;
+      o.res[s] = (const bf16_t*)ep[s].residual;
+      o.act[s] = ep[s].act;
+    }
   }
   HM_REQUIRE(o.col0[n_seg] == N, HM_ERR_INVALID, "segment widths must sum to N");
+  if (dry) return HM_OK;
   const int tiles_m = (M + kGM - 1) / kGM, tiles_n = (N + kGN - 1) / kGN;
-  hipLaunchKernelGGL(linear_bf16, dim3(tiles_m * tiles_n), dim3(256), 0, (hipStream_t)stream,
-                     (const bf16_t*)x, (const bf16_t*)w, M, N, K, o, tiles_n);
-  return hm::check_launch("linear_bf16");
+  hipLaunchKernelGGL(linear_bf16, dim3(tiles_m * tiles_n), dim3(256), 0, st, (const bf16_t*)x,
+                     (const bf16_t*)w, M, N, K, o, tiles_n);
+  return check_launch("linear_bf16");
+}
+
+}  // namespace hm
+
+extern "C" {
+
+hm_status hm_linear_bf16(const void* x, const void* w, int M, int N, int K, int n_seg,
+                         void* const* outs, const int* seg_cols, void* stream) {
+  return hm::linear_launch(x, w, M, N, K, n_seg, outs, seg_cols, nullptr, (hipStream_t)stream);
+}
+
+hm_status hm_linear_bf16_ex(const void* x, const void* w, int M, int N, int K, int n_seg,
+                            void* const* outs, const int* seg_cols,
+                            const hm_linear_epilogue* epilogues, void* stream) {
+  return hm::linear_launch(x, w, M, N, K, n_seg, outs, seg_cols, epilogues, (hipStream_t)stream);
 }
 
 }  // extern "C"

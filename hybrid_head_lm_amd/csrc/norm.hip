@@ -210,9 +210,109 @@ void launch_norm(const void* ya, const void* ys, const float* ba, const float* b
                        (const Tact*)ys, ba, bs, eps, (Tact*)out, rows, width);
 }
 
+// RMS norm with a learned weight (the block's two normalisation layers):
+// out = x / sqrt(mean(x^2) + eps) * w per row.  width % 8 == 0 and width <=
+// 64 * 8 * kMaxC: eight rows per workgroup, one per wave, held in registers;
+// the weight is staged in LDS once per workgroup.
+template <typename Tact>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void rms_norm_rows(
+    const Tact* __restrict__ x, const float* __restrict__ w, float eps, Tact* __restrict__ out,
+    long long rows, int width) {
+  __shared__ float4 sw[64 * kMaxC * 2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * kRowsPerBlock + wave;
+  const bool live = row < rows;
+  const int n8 = width >> 3;
+  const Tact* px = x + row * width;
+  float a[kMaxC][8];
+  if (live) {
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k) {
+      const int c = lane + 64 * k;
+      if (c < n8) Vec8<Tact>::ld(px + 8 * c, a[k]);
+    }
+  }
+  for (int i = threadIdx.x; i < 2 * n8; i += 64 * kRowsPerBlock) sw[i] = ((const float4*)w)[i];
+  __syncthreads();
+  if (!live) return;
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxC; ++k)
+    if (lane + 64 * k < n8)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += a[k][i] * a[k][i];
+  ss = wave_sum(ss);
+  const float r = 1.f / sqrtf(ss / (float)width + eps);
+  Tact* po = out + row * width;
+#pragma unroll
+  for (int k = 0; k < kMaxC; ++k) {
+    const int c = lane + 64 * k;
+    if (c < n8) {
+      const float4 w0 = sw[2 * c], w1 = sw[2 * c + 1];
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = a[k][i] * r * wv[i];
+      Vec8<Tact>::st(po + 8 * c, y);
+    }
+  }
+}
+
+// any width: one wave per row, the row read twice (the second read from L2).
+template <typename Tact>
+__global__ __launch_bounds__(256) void rms_norm_scalar(const Tact* __restrict__ x,
+                                                       const float* __restrict__ w, float eps,
+                                                       Tact* __restrict__ out, long long rows,
+                                                       int width) {
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const Tact* px = x + row * width;
+  float ss = 0.f;
+  for (int c = lane; c < width; c += 64) {
+    const float v = ActIO<Tact>::ld(px + c);
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  const float r = 1.f / sqrtf(ss / (float)width + eps);
+  Tact* po = out + row * width;
+  for (int c = lane; c < width; c += 64) ActIO<Tact>::st(po + c, ActIO<Tact>::ld(px + c) * r * w[c]);
+}
+
 }  // namespace
 
 namespace hm {
+
+hm_status rms_norm_impl(const void* x, const float* w, float eps, void* out, long long rows,
+                        int width, hm_dtype dtype, hipStream_t st, bool dry) {
+  HM_PTR(x);
+  HM_PTR(w);
+  HM_PTR(out);
+  HM_REQUIRE(rows > 0 && width > 0, HM_ERR_INVALID, "rows and width must be positive");
+  HM_REQUIRE(eps >= 0.f && std::isfinite(eps), HM_ERR_INVALID, "eps must be finite and >= 0");
+  HM_REQUIRE(dtype == HM_BF16 || dtype == HM_F32, HM_ERR_UNSUPPORTED, "dtype must be f32 or bf16");
+  HM_REQUIRE(out != x, HM_ERR_INVALID, "out must not alias x");
+  HM_REQUIRE((rows + 3) / 4 < (1LL << 31), HM_ERR_UNSUPPORTED, "too many rows");
+  if (dry) return HM_OK;
+  const bool regs = width % 8 == 0 && width <= 64 * 8 * kMaxC;
+  const dim3 g8((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), g4((unsigned)((rows + 3) / 4));
+  if (dtype == HM_BF16) {
+    if (regs)
+      hipLaunchKernelGGL(rms_norm_rows<bf16_t>, g8, dim3(64 * kRowsPerBlock), 0, st,
+                         (const bf16_t*)x, w, eps, (bf16_t*)out, rows, width);
+    else
+      hipLaunchKernelGGL(rms_norm_scalar<bf16_t>, g4, dim3(256), 0, st, (const bf16_t*)x, w,
+                         eps, (bf16_t*)out, rows, width);
+  } else {
+    if (regs)
+      hipLaunchKernelGGL(rms_norm_rows<float>, g8, dim3(64 * kRowsPerBlock), 0, st,
+                         (const float*)x, w, eps, (float*)out, rows, width);
+    else
+      hipLaunchKernelGGL(rms_norm_scalar<float>, g4, dim3(256), 0, st, (const float*)x, w, eps,
+                         (float*)out, rows, width);
+  }
+  return check_launch("rms_norm");
+}
 
 hm_status norm_mean_impl(const void* ya, const void* ys, const float* beta_a,
                          const float* beta_s, float eps, void* out, long long rows, int width,
@@ -243,4 +343,9 @@ extern "C" hm_status hm_branch_norm_mean(const void* ya, const void* ys, const f
                                          void* stream) {
   return hm::norm_mean_impl(ya, ys, beta_a, beta_s, eps, out, rows, width, dtype,
                             (hipStream_t)stream, false);
+}
+
+extern "C" hm_status hm_rms_norm(const void* x, const float* w, float eps, void* out,
+                                 long long rows, int width, hm_dtype dtype, void* stream) {
+  return hm::rms_norm_impl(x, w, eps, out, rows, width, dtype, (hipStream_t)stream, false);
 }

@@ -7,15 +7,16 @@ instead of keeping their own (Hymba blog, juejin.cn "NVIDIA提出Hymba网络",
 K and laid-out V): the producer layer prepares it, the consumer layer attends
 over it with its own queries and never reads its own K/V.
 
-The projections between layers (W_out, the FFN, W_in of the next layer) are
-outside the mixer core, so every layer here takes its own already-projected
-inputs.
+StackPlan chains mixer cores, each over its own already-projected inputs.
+BlockStack chains whole blocks (norm, projections, mixer, norm, FFN) over one
+hidden-state tensor, as the model does: a block that reuses its neighbour's
+K/V has no K, V projection of its own.
 """
 from __future__ import annotations
 
 import torch
 
-from .api import PrefillPlan
+from .api import BlockPlan, PrefillPlan
 
 
 class StackPlan:
@@ -57,3 +58,36 @@ class StackPlan:
     def run(self):
         for p in self.plans:
             p.run()
+
+
+class BlockStack:
+    """Whole blocks over ``hidden`` [B, T, d_model] (bf16, updated in place).
+    ``layers[i]`` holds block i's weights (see BlockPlan); ``roles[i] =
+    (window, kv_source)`` as for StackPlan.  All blocks share one workspace;
+    every producer block keeps its own prepared K/V buffer."""
+
+    def __init__(self, layers, roles, hidden, Hq: int, Hkv: int, n_meta: int,
+                 rope_base: float = 10000.0, eps: float = 1e-6):
+        if len(layers) != len(roles):
+            raise ValueError("one role per layer")
+        self.hidden = hidden
+        self.plans = []
+        kvs = {}
+        ws = None
+        for i, ((window, src), w) in enumerate(zip(roles, layers)):
+            if src > i:
+                raise ValueError("a block can only reuse the K/V of an earlier block")
+            reuse = src != i
+            if reuse and src not in kvs:
+                raise ValueError(f"block {i} reuses K/V of block {src}, which prepares none")
+            p = BlockPlan(w, hidden, Hq, Hkv, n_meta, window, rope_base=rope_base, eps=eps,
+                          kv=kvs[src] if reuse else None, kv_reuse=reuse, workspace=ws)
+            ws = p.ws
+            if not reuse:
+                kvs[i] = p.kv
+            self.plans.append(p)
+
+    def run(self):
+        for p in self.plans:
+            p.run()
+        return self.hidden

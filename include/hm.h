@@ -12,8 +12,9 @@
  *     (global first/middle/last layers, sliding window elsewhere, adjacent
  *     layers share the KV cache);
  *   - Hymba-1.5B-Base model card, "模型架构" (GQA, RoPE, 16 SSM states).
- * The projections W_in_proj and W_out_proj are outside this library: every
- * call takes already-projected tensors.
+ * The mixer entry points take already-projected tensors; hm_linear_bf16 and
+ * hm_linear_bf16_ex are the projections around them, and hm_block_prefill
+ * runs a whole block (norm, projections, mixer, norm, feed-forward network).
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless stated otherwise; tensors are
@@ -165,13 +166,45 @@ hm_status hm_branch_norm_mean(const void* ya, const void* ys, const float* beta_
  *   y = x W^T: x [M, K] bf16, w [N, K] bf16 (nn.Linear layout), float32
  *   accumulation, results rounded to bf16.
  * The N output columns are split into n_seg consecutive segments: segment s
- * has seg_cols[s] columns (a positive multiple of 32) and is written to
+ * has seg_cols[s] columns (a positive multiple of 16) and is written to
  * outs[s] as [M, seg_cols[s]], so an in-projection writes Q, K, V, x and z
  * into their own tensors.  outs and seg_cols are HOST arrays of n_seg
  * entries (1 <= n_seg <= 8; widths summing to N).  K must be a multiple of 64.
  * ---------------------------------------------------------------------- */
 hm_status hm_linear_bf16(const void* x, const void* w, int M, int N, int K, int n_seg,
                          void* const* outs, const int* seg_cols, void* stream);
+
+/* ------------------------------------------------------------------------
+ * hm_linear_bf16 with an epilogue per output segment, applied in float32
+ * before the bf16 rounding:
+ *   y = act(x W^T + bias) + residual
+ * act: HM_ACT_NONE; HM_ACT_SILU, v / (1 + e^-v) (the feed-forward network's
+ * hidden layer); HM_ACT_SOFTPLUS, log(1 + e^v) (non-negative SSM step sizes).
+ * bias: [width] f32 or NULL.  residual: [M, width] bf16 or NULL; it may be the
+ * segment's own output (an in-place skip connection, y += ...), but no other
+ * segment's output, x or w.  epilogues: HOST array of n_seg entries, or NULL
+ * (then identical to hm_linear_bf16).  Other arguments and errors as for
+ * hm_linear_bf16.
+ * ---------------------------------------------------------------------- */
+typedef enum { HM_ACT_NONE = 0, HM_ACT_SILU = 1, HM_ACT_SOFTPLUS = 2 } hm_act;
+typedef struct {
+  const float* bias;     /* [width] f32 or NULL */
+  const void* residual;  /* [M, width] bf16 or NULL */
+  int act;               /* hm_act */
+} hm_linear_epilogue;
+hm_status hm_linear_bf16_ex(const void* x, const void* w, int M, int N, int K, int n_seg,
+                            void* const* outs, const int* seg_cols,
+                            const hm_linear_epilogue* epilogues, void* stream);
+
+/* ------------------------------------------------------------------------
+ * RMS norm with a learned weight: the two normalisation layers of a Hymba
+ * block (Hymba blog, "Hymba 的整体架构": a block normalises its input before
+ * the hybrid-head module and again before the feed-forward network).
+ *   out[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * w
+ * x, out: [rows, width] (act dtype, out must not alias x); w: [width] f32.
+ * ---------------------------------------------------------------------- */
+hm_status hm_rms_norm(const void* x, const float* w, float eps, void* out, long long rows,
+                      int width, hm_dtype dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * One whole mixer layer in prefill: attention and the SSM branch
@@ -233,6 +266,55 @@ typedef struct {
 } hm_prefill_args;
 hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream);
 size_t hm_mixer_prefill_workspace(const hm_prefill_args* a);
+
+/* ------------------------------------------------------------------------
+ * One whole Hymba block in prefill, over the hidden states of X~ (Hymba blog,
+ * "Hymba 的整体架构": normalisation, hybrid-head module, normalisation,
+ * feed-forward network; "数学表示" §2 and §5: in- and out-projection; model
+ * card, "模型架构": FFN width 5504).  With pre-norm skip connections:
+ *   u = rms_norm(h, ln1)
+ *   [q, k, v, x, z] = u W_in^T        (consumer: [q, x, z]; K, V reused)
+ *   [dt, B, C] = x W_dbc^T;  delta = softplus(dt + dt_bias)
+ *   m = mixer(q, k, v, x, delta, B, C, z)      (as hm_mixer_prefill)
+ *   h1 = h + m W_out^T
+ *   h2 = h1 + W_down SiLU(W_up rms_norm(h1, ln2))
+ * hidden [B, T, d_model] holds h on entry and h2 on return (in place).
+ * Weights (bf16, nn.Linear layout [out, in]): w_in [Hq*Dh + 2*Hkv*Dh + 2*Di,
+ * d_model] (rows Q, K, V, x, z), or [Hq*Dh + 2*Di, d_model] (rows Q, x, z)
+ * when kv_reuse != 0; w_dbc [Di + 2*N, Di] (rows dt, B, C); w_out [d_model,
+ * Di]; w_up [d_ffn, d_model]; w_down [d_model, d_ffn].  f32 vectors: ln1, ln2
+ * [d_model]; dt_bias [Di]; A, D, conv_w, conv_b, beta_a, beta_s as for
+ * hm_mixer_prefill.  eps is used by all four RMS norms.
+ * Prepared K/V (the adjacent-layer sharing): kv_reuse == 0 prepares this
+ * block's K, V into kv (hm_attn_kv_bytes(B, T, Hkv, Dh, dtype) bytes; NULL:
+ * into the workspace); kv_reuse != 0 attends over kv as an earlier block
+ * with the same B, T, Hkv, Dh, rope_base and pos0 left it.
+ * Supported: bf16, Dh = 64, N = 16, K = 4, d_model and d_ffn multiples of 64
+ * (else HM_ERR_UNSUPPORTED).  Workspace: hm_block_prefill_workspace() bytes
+ * (the block's intermediate activations and the mixer's workspace); blocks
+ * that run one after the other on one stream may share it.  Launches: two
+ * norms, five matrix products and the mixer's three, all on `stream`.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int B, T, d_model, d_ffn, Hq, Hkv, Dh, Di, N, K, n_meta, window;
+  long long pos0;
+  float rope_base, scale, eps;
+  hm_dtype dtype;
+  void* hidden;                               /* [B, T, d_model] in/out */
+  const float *ln1, *ln2;                     /* [d_model] */
+  const void *w_in, *w_dbc;                   /* see above */
+  const float* dt_bias;                       /* [Di] */
+  const float *A, *D, *conv_w, *conv_b;       /* [Di,N], [Di], [Di,K], [Di] */
+  const float *beta_a, *beta_s;               /* [Di] */
+  const void *w_out, *w_up, *w_down;          /* see above */
+  void* kv;                                   /* prepared K/V, see above */
+  size_t kv_bytes;
+  int kv_reuse;
+  void* workspace;
+  size_t workspace_bytes;
+} hm_block_args;
+hm_status hm_block_prefill(const hm_block_args* a, void* stream);
+size_t hm_block_prefill_workspace(const hm_block_args* a);
 
 /* ------------------------------------------------------------------------
  * One decode token per sequence through ONE layer of an adjacent pair that

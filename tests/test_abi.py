@@ -155,29 +155,31 @@ def test_prefill_cached_meta_rejects_unsupported_modes():
 
 
 def test_ctypes_structs_match_the_header(tmp_path):
-    """The binding's hm_prefill_args / hm_step_args layouts equal the C ones."""
+    """The binding's argument-struct layouts equal the C ones."""
     import shutil
     import subprocess
     cxx = shutil.which("g++") or shutil.which("c++")
     if cxx is None:
         pytest.skip("no host C++ compiler")
+    pairs = [(hm.PrefillArgs, "hm_prefill_args"), (hm.StepArgs, "hm_step_args"),
+             (hm.BlockArgs, "hm_block_args"), (hm.LinearEpilogue, "hm_linear_epilogue")]
     src = tmp_path / "sz.cpp"
-    fields_p = [f for f, _ in hm.PrefillArgs._fields_]
-    fields_s = [f for f, _ in hm.StepArgs._fields_]
-    lines = ['#include "hm.h"', "#include <cstdio>", "#include <cstddef>", "int main() {",
-             'printf("%zu %zu\\n", sizeof(hm_prefill_args), sizeof(hm_step_args));']
-    lines += [f'printf("%zu\\n", offsetof(hm_prefill_args, {f}));' for f in fields_p]
-    lines += [f'printf("%zu\\n", offsetof(hm_step_args, {f}));' for f in fields_s]
+    lines = ['#include "hm.h"', "#include <cstdio>", "#include <cstddef>", "int main() {"]
+    for cls, cname in pairs:
+        lines.append(f'printf("%zu\\n", sizeof({cname}));')
+        lines += [f'printf("%zu\\n", offsetof({cname}, {f}));' for f, _ in cls._fields_]
     lines += ["return 0; }"]
     src.write_text("\n".join(lines))
     exe = tmp_path / "sz"
     subprocess.run([cxx, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
-    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
-    vals = [int(v) for v in out]
-    assert vals[0] == ctypes.sizeof(hm.PrefillArgs) and vals[1] == ctypes.sizeof(hm.StepArgs)
-    offs = vals[2:]
-    assert offs[:len(fields_p)] == [getattr(hm.PrefillArgs, f).offset for f in fields_p]
-    assert offs[len(fields_p):] == [getattr(hm.StepArgs, f).offset for f in fields_s]
+    vals = [int(v) for v in
+            subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    for cls, cname in pairs:
+        n = len(cls._fields_)
+        assert vals[0] == ctypes.sizeof(cls), cname
+        assert vals[1:1 + n] == [getattr(cls, f).offset for f, _ in cls._fields_], cname
+        vals = vals[1 + n:]
+    assert vals == []
 
 
 def test_empty_extents_are_rejected():
@@ -214,9 +216,79 @@ def test_linear_rejects_bad_arguments():
     x, w = ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20)
     assert L.hm_linear_bf16(x, w, 8, 96, 100, 2, outs, widths, None) == hm.HM_ERR_UNSUPPORTED
     assert L.hm_linear_bf16(x, w, 8, 95, 64, 2, outs, widths, None) == hm.HM_ERR_INVALID
-    bad = (ctypes.c_int * 2)(48, 48)                  # not multiples of 32
+    bad = (ctypes.c_int * 2)(40, 56)                  # not multiples of 16
     assert L.hm_linear_bf16(x, w, 8, 96, 64, 2, outs, bad, None) == hm.HM_ERR_INVALID
     assert L.hm_linear_bf16(x, w, 0, 96, 64, 2, outs, widths, None) == hm.HM_ERR_INVALID
     assert L.hm_linear_bf16(x, w, 8, 96, 64, 9, outs, widths, None) == hm.HM_ERR_INVALID
     alias = (ctypes.c_void_p * 2)(1 << 20, 4 << 20)   # output aliases x
     assert L.hm_linear_bf16(x, w, 8, 96, 64, 2, alias, widths, None) == hm.HM_ERR_INVALID
+
+
+def test_linear_epilogues_reject_bad_arguments():
+    L = hm.lib
+    outs = (ctypes.c_void_p * 2)(3 << 20, 4 << 20)
+    widths = (ctypes.c_int * 2)(16, 80)
+    x, w = ctypes.c_void_p(1 << 20), ctypes.c_void_p(2 << 20)
+    ep = (hm.LinearEpilogue * 2)()
+    ep[0].act = 7                                      # unknown activation
+    assert L.hm_linear_bf16_ex(x, w, 8, 96, 64, 2, outs, widths, ep, None) == hm.HM_ERR_INVALID
+    ep[0].act = hm.HM_ACT_SILU
+    ep[1].residual = 3 << 20                           # another segment's output
+    assert L.hm_linear_bf16_ex(x, w, 8, 96, 64, 2, outs, widths, ep, None) == hm.HM_ERR_INVALID
+    ep[1].residual = 1 << 20                           # x
+    assert L.hm_linear_bf16_ex(x, w, 8, 96, 64, 2, outs, widths, ep, None) == hm.HM_ERR_INVALID
+    same = (ctypes.c_void_p * 2)(3 << 20, 3 << 20)     # two segments, one tensor
+    assert L.hm_linear_bf16_ex(x, w, 8, 96, 64, 2, same, widths, None, None) == hm.HM_ERR_INVALID
+
+
+def test_rms_norm_rejects_bad_arguments():
+    L = hm.lib
+    x, wv, o = (ctypes.c_void_p(i << 20) for i in range(1, 4))
+    assert L.hm_rms_norm(x, wv, 1e-6, o, 0, 64, hm.HM_BF16, None) == hm.HM_ERR_INVALID
+    assert L.hm_rms_norm(x, wv, 1e-6, o, 4, 0, hm.HM_BF16, None) == hm.HM_ERR_INVALID
+    assert L.hm_rms_norm(x, wv, -1.0, o, 4, 64, hm.HM_BF16, None) == hm.HM_ERR_INVALID
+    assert L.hm_rms_norm(x, wv, 1e-6, x, 4, 64, hm.HM_BF16, None) == hm.HM_ERR_INVALID
+    assert L.hm_rms_norm(x, wv, 1e-6, o, 4, 64, 5, None) == hm.HM_ERR_UNSUPPORTED
+
+
+def _block_args(**kw):
+    a = hm.BlockArgs(B=1, T=200, d_model=192, d_ffn=320, Hq=4, Hkv=2, Dh=64, Di=256, N=16, K=4,
+                     n_meta=8, window=64, rope_base=1e4, eps=1e-6, dtype=hm.HM_BF16)
+    for f in ("hidden", "ln1", "ln2", "w_in", "w_dbc", "dt_bias", "A", "D", "conv_w", "conv_b",
+              "beta_a", "beta_s", "w_out", "w_up", "w_down"):
+        setattr(a, f, FAKE.value)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_block_workspace_and_rejections():
+    L = hm.lib
+    a = _block_args()
+    nb = L.hm_block_prefill_workspace(ctypes.byref(a))
+    R = 200
+    # at least the block's own tensors (norm output, Q, K, V, x, z, step sizes, B, C,
+    # both branch outputs, the mixer output) and the prepared K/V held in the workspace
+    assert nb >= R * 2 * (192 + 256 + 2 * 128 + 256 * 3 + 2 * 16 + 3 * 256) + 2 * 2 * 256 * 64 * 2
+    a.workspace, a.workspace_bytes = 5 << 20, nb
+    cases = [
+        (dict(dtype=hm.HM_F32), hm.HM_ERR_UNSUPPORTED),
+        (dict(d_ffn=330), hm.HM_ERR_UNSUPPORTED),
+        (dict(d_model=100), hm.HM_ERR_UNSUPPORTED),
+        (dict(Dh=32, Di=128), hm.HM_ERR_UNSUPPORTED),
+        (dict(Di=200), hm.HM_ERR_INVALID),
+        (dict(T=0), hm.HM_ERR_INVALID),
+        (dict(B=0), hm.HM_ERR_INVALID),
+        (dict(kv_reuse=1), hm.HM_ERR_INVALID),
+        (dict(w_up=None), hm.HM_ERR_INVALID),
+        (dict(ln2=(1 << 20) + 4), hm.HM_ERR_INVALID),
+        (dict(workspace_bytes=nb - 256), hm.HM_ERR_WORKSPACE),
+        (dict(workspace=None), hm.HM_ERR_WORKSPACE),
+    ]
+    for kw, want in cases:
+        b = _block_args(workspace=5 << 20, workspace_bytes=nb)
+        for k, v in kw.items():
+            setattr(b, k, v)
+        assert L.hm_block_prefill(ctypes.byref(b), None) == want, (kw, _err())
+    assert L.hm_block_prefill(None, None) == hm.HM_ERR_INVALID
+    assert L.hm_block_prefill_workspace(ctypes.byref(_block_args(T=0))) == 0
