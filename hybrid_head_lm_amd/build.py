@@ -33,9 +33,20 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+# Files whose kernels keep MFMA accumulators in AGPRs (more than 256 of them
+# per lane): built without the VGPR-only MFMA form.
+AGPR_FILES = {"linear_w4.hip"}
+
+
+def _flags(src: str):
+    if os.path.basename(src) in AGPR_FILES:
+        return [f for f in CFLAGS if f not in ("-mllvm", "-amdgpu-mfma-vgpr-form=true")]
+    return CFLAGS
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *_flags(src), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)

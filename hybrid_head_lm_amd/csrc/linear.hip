@@ -3,6 +3,8 @@
 // §5: W_out_proj maps the fused output back).  y = x W^T with the weight in
 // nn.Linear layout [N, K], bf16 operands, float32 accumulation, bf16 results.
 //
+// Problems of at least 192 tiles of 256 x 256 run the 4-wave 256 x 256 kernel
+// of linear_w4.hip; smaller ones run the kernel here.
 // One workgroup of 4 waves per 128 x 128 output tile; 64-wide K steps of x and
 // W go HBM -> LDS with global_load_lds (double buffered, 2 x 32 KB, so two
 // workgroups share a CU); each wave owns a 64 x 64 quarter as 2 x 2 blocks of
@@ -16,32 +18,17 @@
 #include <algorithm>
 #include <cmath>
 
-#include "hm_common.h"
+#include "linear_dev.h"
 
 namespace {
 
+using namespace hm_lin;
+
 constexpr int kGM = 128, kGN = 128, kGK = 64;   // workgroup tile (rows, columns, K step)
-constexpr int kMaxSeg = 8;
-
-struct LinOut {
-  bf16_t* p[kMaxSeg];          // segment outputs, [M, col0[s+1] - col0[s]]
-  const float* bias[kMaxSeg];  // per segment: [width] f32 or null
-  const bf16_t* res[kMaxSeg];  // per segment: [M, width] or null (may be p[s] itself)
-  int act[kMaxSeg];            // per segment: HM_ACT_*
-  int col0[kMaxSeg + 1];       // segment s holds the output columns [col0[s], col0[s+1])
-  int n;                       // segments
-};
-
-// v + bias, then the activation, then + residual, in float32.
-HM_DEV float lin_act(float v, int act) {
-  if (act == HM_ACT_SILU) return v / (1.f + __expf(-v));
-  if (act == HM_ACT_SOFTPLUS) return v > 20.f ? v : log1pf(__expf(v));
-  return v;
-}
+constexpr int kBigTilesMin = 192;               // 256 x 256 tiles from this many on
 
 HM_DEV int lin_slot(int row, int c) { return c ^ ((row >> 1) & 7); }
 HM_DEV int lin_off(int row, int c) { return row * 128 + (lin_slot(row, c) << 4); }
-typedef __attribute__((address_space(3))) void lin_lds_t;
 
 __global__ __launch_bounds__(256) void linear_bf16(const bf16_t* __restrict__ x,
                                                    const bf16_t* __restrict__ w, int M, int N,
@@ -122,14 +109,13 @@ __global__ __launch_bounds__(256) void linear_bf16(const bf16_t* __restrict__ x,
   for (int j = 0; j < 2; ++j) {
     const int col = n0 + 64 * wc + 32 * j + r32;
     if (col >= N) continue;
-    int s = 0;
-    while (s + 1 < out.n && col >= out.col0[s + 1]) ++s;
-    bf16_t* dst = out.p[s];
-    const bf16_t* res = out.res[s];
-    const int act = out.act[s];
-    const int ld = out.col0[s + 1] - out.col0[s];
-    const int cn = col - out.col0[s];
-    const float bv = out.bias[s] ? out.bias[s][cn] : 0.f;
+    const SegPick sp = pick_segment(out, col);
+    bf16_t* dst = sp.dst;
+    const bf16_t* res = sp.res;
+    const int act = sp.act;
+    const int ld = sp.ld;
+    const int cn = col - sp.c0;
+    const float bv = sp.bias ? sp.bias[cn] : 0.f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -148,6 +134,8 @@ __global__ __launch_bounds__(256) void linear_bf16(const bf16_t* __restrict__ x,
 }  // namespace
 
 namespace hm {
+
+using namespace hm_lin;
 
 // Validates the arguments, then one launch.
 hm_status linear_launch(const void* x, const void* w, int M, int N, int K, int n_seg,
@@ -180,6 +168,7 @@ hm_status linear_launch(const void* x, const void* w, int M, int N, int K, int n
                  HM_ERR_INVALID, "unknown activation");
       HM_REQUIRE(ep[s].residual == nullptr || (ep[s].residual != x && ep[s].residual != w),
                  HM_ERR_INVALID, "a residual must not alias x or w");
+      HM_OPT_PTR(ep[s].residual);
       for (int t = 0; t < n_seg; ++t)
         HM_REQUIRE(ep[s].residual == nullptr || t == s || ep[s].residual != outs[t],
                    HM_ERR_INVALID, "a residual may only alias its own segment's output");
@@ -190,6 +179,13 @@ hm_status linear_launch(const void* x, const void* w, int M, int N, int K, int n
   }
   HM_REQUIRE(o.col0[n_seg] == N, HM_ERR_INVALID, "segment widths must sum to N");
   if (dry) return HM_OK;
+  // 256 x 256 tiles (linear_w4.hip) once they fill most CUs; else 128 x 128
+  // tiles (two workgroups per CU).
+  const int big_m = (M + 255) / 256, big_n = (N + 255) / 256;
+  if (big_m * big_n >= kBigTilesMin) {
+    launch_w4((const bf16_t*)x, (const bf16_t*)w, M, N, K, o, st);
+    return check_launch("linear_bf16_w4");
+  }
   const int tiles_m = (M + kGM - 1) / kGM, tiles_n = (N + kGN - 1) / kGN;
   hipLaunchKernelGGL(linear_bf16, dim3(tiles_m * tiles_n), dim3(256), 0, st, (const bf16_t*)x,
                      (const bf16_t*)w, M, N, K, o, tiles_n);

@@ -1,0 +1,52 @@
+// Pieces shared by the projection kernels (bf16 MFMA GEMM, y = x W^T with the
+// weight in nn.Linear layout [N, K]): the per-segment output description and
+// epilogue, and the launch of the 4-wave 256 x 256 tile kernel.
+#pragma once
+
+#include "hm_common.h"
+
+namespace hm_lin {
+
+constexpr int kMaxSeg = 8;
+typedef __attribute__((address_space(3))) void lin_lds_t;
+
+struct LinOut {
+  bf16_t* p[kMaxSeg];          // segment outputs, [M, col0[s+1] - col0[s]]
+  const float* bias[kMaxSeg];  // per segment: [width] f32 or null
+  const bf16_t* res[kMaxSeg];  // per segment: [M, width] or null (may be p[s] itself)
+  int act[kMaxSeg];            // per segment: HM_ACT_*
+  int col0[kMaxSeg + 1];       // segment s holds the output columns [col0[s], col0[s+1])
+  int n;                       // segments
+};
+
+// The segment holding output column `col`, chosen with compile-time indices
+// only (a lane-varying index into the argument struct would copy it to
+// scratch memory).
+struct SegPick {
+  bf16_t* dst;
+  const bf16_t* res;
+  const float* bias;
+  int act, c0, ld;
+};
+HM_DEV SegPick pick_segment(const LinOut& out, int col) {
+  SegPick p{out.p[0], out.res[0], out.bias[0], out.act[0], 0, out.col0[1]};
+#pragma unroll
+  for (int q = 1; q < kMaxSeg; ++q)
+    if (q < out.n && col >= out.col0[q])
+      p = SegPick{out.p[q], out.res[q], out.bias[q], out.act[q], out.col0[q],
+                  out.col0[q + 1] - out.col0[q]};
+  return p;
+}
+
+// v + bias, then the activation, then + residual, in float32.
+HM_DEV float lin_act(float v, int act) {
+  if (act == HM_ACT_SILU) return v / (1.f + __expf(-v));
+  if (act == HM_ACT_SOFTPLUS) return v > 20.f ? v : log1pf(__expf(v));
+  return v;
+}
+
+// 256 x 256 tiles, 4 waves (linear_w4.hip).  Arguments validated by the caller.
+void launch_w4(const bf16_t* x, const bf16_t* w, int M, int N, int K, const LinOut& out,
+               hipStream_t st);
+
+}  // namespace hm_lin

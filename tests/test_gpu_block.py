@@ -53,7 +53,7 @@ def test_rms_norm(rows, width, dtype):
 
 
 @pytest.mark.parametrize("M,K,segs", [(300, 192, [16, 48, 64]), (2176, 1600, [1600, 16, 16]),
-                                      (77, 64, [80])])
+                                      (77, 64, [80]), (4100, 320, [1600, 16, 2384])])
 def test_linear_epilogues(M, K, segs):
     """softplus(. + bias) on the first segment, SiLU on the second, an in-place
     residual on the last (the block's step sizes, FFN and skip connections)."""

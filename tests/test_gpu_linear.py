@@ -23,7 +23,11 @@ def setup_module(module):
 @pytest.mark.parametrize("M,K,segs", [(2176, 1600, [1600, 320, 320, 1600, 1600]),
                                       (2176, 1600, [1600]), (77, 64, [32, 64]),
                                       (1, 128, [32]), (300, 192, [128, 32, 96]),
-                                      (129, 320, [160, 160])])
+                                      (129, 320, [160, 160]),
+                                      # 256 x 256 tiles (ragged in both directions)
+                                      (4100, 320, [1600, 16, 2384]), (8192, 64, [4096]),
+                                      # 192 tiles (the 256 x 256 kernel) and 189 (128 x 128)
+                                      (3000, 128, [16, 4080]), (2304, 64, [5376])])
 def test_linear_bf16(M, K, segs):
     rng = np.random.default_rng(M + K)
     x = bf16_round(rng.standard_normal((M, K)))
