@@ -100,34 +100,58 @@ __global__ __launch_bounds__(256) void linear_bf16(const bf16_t* __restrict__ x,
     }
   }
 
-  // Output: element r of block (i, j) is row 32 i + 8 (r / 4) + 4 hk + r % 4 and
-  // column 32 j + lane % 32 of the quarter.  Each lane finds the segment of
-  // its own column (segment widths are multiples of 16, so a 32-column block
-  // may straddle two).  A residual that is the output itself is read and
-  // written by the same lane.
+  // Output through LDS (the operand stages are idle now): element r of block
+  // (i, j) is row 32 i + 8 (r / 4) + 4 hk + r % 4 and column 32 j + lane % 32
+  // of the wave's quarter.  The tile is staged as float32, column c of row r
+  // at c ^ (32 ((r >> 2) & 1)) so that the two row groups of a block write
+  // disjoint banks; then every thread takes 16-byte chunks (8 columns of one
+  // row, one segment): bias, activation, residual, bf16.
+  float* stg = (float*)&smem[0][0][0];
+  __syncthreads();   // every wave is done with the operand stages
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = n0 + 64 * wc + 32 * j + r32;
-    if (col >= N) continue;
-    const SegPick sp = pick_segment(out, col);
-    bf16_t* dst = sp.dst;
-    const bf16_t* res = sp.res;
-    const int act = sp.act;
-    const int ld = sp.ld;
-    const int cn = col - sp.c0;
-    const float bv = sp.bias ? sp.bias[cn] : 0.f;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + 64 * wr + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
-        if (row < M) {
-          const size_t e = (size_t)row * ld + cn;
-          float v = lin_act(acc[i][j][r] + bv, act);
-          if (res) v += bf2f(res[e]);
-          dst[e] = f2bf(v);
-        }
+        const int sr = 64 * wr + 32 * i + 8 * (r >> 2) + 4 * hk + (r & 3);
+        stg[sr * 128 + ((64 * wc + 32 * j + r32) ^ (hk << 5))] = acc[i][j][r];
       }
+  __syncthreads();
+#pragma unroll 2
+  for (int it = 0; it < 8; ++it) {
+    const int q = it * 256 + tid, sr = q >> 4, c = q & 15;
+    const int row = m0 + sr, col = n0 + 8 * c;
+    if (row >= M || col >= N) continue;
+    const float* sp8 = stg + sr * 128 + ((8 * c) ^ (((sr >> 2) & 1) << 5));
+    const float4 v0 = *(const float4*)sp8, v1 = *(const float4*)(sp8 + 4);
+    float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const SegPick sp = pick_segment(out, col);
+    const int cn = col - sp.c0;
+    if (sp.bias) {
+      const float4 b0 = *(const float4*)(sp.bias + cn), b1 = *(const float4*)(sp.bias + cn + 4);
+      v[0] += b0.x; v[1] += b0.y; v[2] += b0.z; v[3] += b0.w;
+      v[4] += b1.x; v[5] += b1.y; v[6] += b1.z; v[7] += b1.w;
+    }
+    if (sp.act != HM_ACT_NONE)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = lin_act(v[k], sp.act);
+    const size_t e = (size_t)row * sp.ld + cn;
+    if (sp.res) {
+      const uint4 rr = *(const uint4*)(sp.res + e);
+      const uint32_t rw[4] = {rr.x, rr.y, rr.z, rr.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] += __uint_as_float(rw[k] << 16);
+        v[2 * k + 1] += __uint_as_float(rw[k] & 0xffff0000u);
+      }
+    }
+    uint4 o;
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    o.z = pack_bf16x2(v[4], v[5]);
+    o.w = pack_bf16x2(v[6], v[7]);
+    *(uint4*)(sp.dst + e) = o;
   }
 }
 
