@@ -22,6 +22,12 @@ Also reported on the same JSON line:
                 global, adjacent sliding-window layers sharing prepared K/V);
   ragged_decode the decode pair with one n_prev per sequence (warm);
   projections   the in- and out-projections around the layer (bf16 MFMA GEMM);
+  block         one whole Hymba block (RMS norm, in-projection, step-size/B/C
+                projection, the mixer, out-projection with the skip connection,
+                RMS norm, FFN 1600 -> 5504 -> 1600 with the skip connection) over
+                the same rows at the model card's widths;
+  block_stack   32 whole blocks chained over one hidden-state tensor at the
+                stack's size (batch 2, 128 + 16384 tokens; KV shared as above);
   cached_meta   the same layer with the meta tokens' K/V and SSM states taken
                 from a cache: only the 2048 real-token rows are computed
                 (real tokens/s, beside the full layer's real tokens/s);
@@ -256,6 +262,37 @@ def run_stack(shape, hm, steps, warmup):
     return ms, len(roles)
 
 
+def block_matmul_flops(shape, producer: bool = True) -> float:
+    """Dense products of one block: in-projection, the step-size/B/C
+    projection, out-projection and the two FFN matrices (2 flops per MAC)."""
+    from workloads import block_weight_rows
+    R = shape.B * shape.T
+    macs = (shape.d_model * block_weight_rows(shape, producer)
+            + shape.Di * (shape.Di + 2 * shape.Ns) + shape.Di * shape.d_model
+            + 2 * shape.d_model * shape.d_ffn)
+    return 2.0 * R * macs
+
+
+def run_blocks(shape, hm, n_layers, steps, warmup):
+    """Whole blocks (norm, projections, mixer, norm, FFN) chained over one
+    hidden-state tensor; weights from the device generator.  Returns ms per
+    pass and the pass's dense-product and attention flops."""
+    import torch
+    from workloads import block_inputs_torch, stack_layer_roles, with_
+    dev = torch.device("cuda")
+    roles = stack_layer_roles(with_(shape, layers=n_layers)) if n_layers > 1 else [(shape.W, 0)]
+    layers = [block_inputs_torch(shape, 0, l, src == l, dev, hidden=(l == 0))
+              for l, (_, src) in enumerate(roles)]
+    hidden = layers[0].pop("hidden")
+    stack = hm.BlockStack(layers, roles, hidden, shape.Hq, shape.Hkv, shape.M, shape.rope_base,
+                          shape.eps)
+    ms = timed(stack.run, steps, warmup)
+    fl_mm = sum(block_matmul_flops(shape, src == l) for l, (_, src) in enumerate(roles))
+    fl_at = sum(attn_flops(with_(shape, W=w)) for w, _ in roles)
+    del stack, layers, hidden
+    return ms, len(roles), fl_mm, fl_at
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -275,8 +312,8 @@ def main():
     import numpy as np
     import torch
     import hybrid_head_lm_amd as hm
-    from workloads import (DECODE_PAIR, GLOBAL_PREFILL, STACK, SWA_PREFILL, decode_inputs,
-                           prefill_inputs, to_device)
+    from workloads import (BLOCK_STACK, BLOCK_SWA, DECODE_PAIR, GLOBAL_PREFILL, STACK,
+                           SWA_PREFILL, decode_inputs, prefill_inputs, to_device)
 
     torch.cuda.set_device(0)
     shape = SWA_PREFILL
@@ -504,6 +541,17 @@ def main():
     }
     del pa, pb, d
 
+    # one whole block at the model card's widths over the same rows
+    bshape = BLOCK_SWA
+    bms, _, bfl_mm, bfl_at = run_blocks(bshape, hm, 1, args.steps, args.warmup)
+    result["block"] = {
+        "workload": bshape.name + " (width 1600, FFN 5504; norm, projections, mixer, norm, FFN)",
+        "tokens_per_s": bshape.B * bshape.T / (bms * 1e-3), "ms_per_block": bms,
+        "mixer_ms": ms, "matmul_tflop": bfl_mm / 1e12,
+        "tflops": (bfl_mm + bfl_at) / (bms * 1e-3) / 1e12,
+        "frac_mfma": (bfl_mm + bfl_at) / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    torch.cuda.empty_cache()
+
     if not args.quick:
         gshape = GLOBAL_PREFILL
         gt = to_device(prefill_inputs(gshape, 0), gshape.dtype)
@@ -524,6 +572,16 @@ def main():
                            "tokens_per_s_per_layer": STACK.B * STACK.T * nl / (sms * 1e-3),
                            "ms_per_stack": sms,
                            "inputs": "torch Philox generator on the device (same distributions)"}
+        torch.cuda.empty_cache()
+        kms, kl, kfl_mm, kfl_at = run_blocks(BLOCK_STACK, hm, BLOCK_STACK.layers, 3, 1)
+        result["block_stack"] = {
+            "workload": BLOCK_STACK.name + " (32 whole blocks, width 1600, FFN 5504)",
+            "layers": kl, "ms_per_stack": kms,
+            "tokens_per_s_per_layer": BLOCK_STACK.B * BLOCK_STACK.T * kl / (kms * 1e-3),
+            "tokens_per_s": BLOCK_STACK.B * BLOCK_STACK.T / (kms * 1e-3),
+            "tflops": (kfl_mm + kfl_at) / (kms * 1e-3) / 1e12,
+            "frac_mfma": (kfl_mm + kfl_at) / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "inputs": "torch Philox generator on the device (same distributions)"}
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
