@@ -193,6 +193,7 @@ hm_status linear_launch(const void* x, const void* w, int M, int N, int K, int n
       HM_REQUIRE(ep[s].residual == nullptr || (ep[s].residual != x && ep[s].residual != w),
                  HM_ERR_INVALID, "a residual must not alias x or w");
       HM_OPT_PTR(ep[s].residual);
+      HM_OPT_PTR(ep[s].bias);
       for (int t = 0; t < n_seg; ++t)
         HM_REQUIRE(ep[s].residual == nullptr || t == s || ep[s].residual != outs[t],
                    HM_ERR_INVALID, "a residual may only alias its own segment's output");

@@ -180,7 +180,8 @@ hm_status hm_linear_bf16(const void* x, const void* w, int M, int N, int K, int 
  *   y = act(x W^T + bias) + residual
  * act: HM_ACT_NONE; HM_ACT_SILU, v / (1 + e^-v) (the feed-forward network's
  * hidden layer); HM_ACT_SOFTPLUS, log(1 + e^v) (non-negative SSM step sizes).
- * bias: [width] f32 or NULL.  residual: [M, width] bf16 or NULL; it may be the
+ * bias: [width] f32 (16-byte aligned) or NULL.  residual: [M, width] bf16
+ * (16-byte aligned) or NULL; it may be the
  * segment's own output (an in-place skip connection, y += ...), but no other
  * segment's output, x or w.  epilogues: HOST array of n_seg entries, or NULL
  * (then identical to hm_linear_bf16).  Other arguments and errors as for
