@@ -237,6 +237,12 @@ def test_linear_epilogues_reject_bad_arguments():
     assert L.hm_linear_bf16_ex(x, w, 8, 96, 64, 2, outs, widths, ep, None) == hm.HM_ERR_INVALID
     ep[1].residual = 1 << 20                           # x
     assert L.hm_linear_bf16_ex(x, w, 8, 96, 64, 2, outs, widths, ep, None) == hm.HM_ERR_INVALID
+    ep[1].residual = None
+    ep[0].bias = (1 << 20) + 4                         # misaligned bias
+    assert L.hm_linear_bf16_ex(x, w, 8, 96, 64, 2, outs, widths, ep, None) == hm.HM_ERR_INVALID
+    ep[0].bias = None
+    ep[1].residual = (4 << 20) + 8                     # misaligned residual
+    assert L.hm_linear_bf16_ex(x, w, 8, 96, 64, 2, outs, widths, ep, None) == hm.HM_ERR_INVALID
     same = (ctypes.c_void_p * 2)(3 << 20, 3 << 20)     # two segments, one tensor
     assert L.hm_linear_bf16_ex(x, w, 8, 96, 64, 2, same, widths, None, None) == hm.HM_ERR_INVALID
 
