@@ -38,8 +38,10 @@ Also reported on the same JSON line:
                 non-packed fp32 VALU rate (single-pass VALU work per
                 token-channel);
   cpu_baseline  the float64 CPU oracle on one whole layer of the step's workload.
-HBM traffic (`traffic`) of the attention kernel, the SSM branch and the decode
-pair comes from the committed rocprofv3 counter summaries in profiles/ (null
+HBM traffic (`traffic`) of the attention kernel, the SSM branch, the decode pair
+and the block stack's in-projection GEMM (block_stack.roofline, the block's
+dominant kernel timed on its own) comes from the committed rocprofv3 counter
+summaries in profiles/ (null
 once the kernel sources differ from those the counters were taken with);
 `--counters` is the run those summaries are taken over.
 
@@ -67,6 +69,8 @@ ATTN_SOURCES = ("hybrid_head_lm_amd/csrc/attn_dev.h", "hybrid_head_lm_amd/csrc/a
 SSM_SOURCES = ("hybrid_head_lm_amd/csrc/ssm_dev.h", "hybrid_head_lm_amd/csrc/ssm.hip",
                "hybrid_head_lm_amd/csrc/hm_common.h")
 STEP_SOURCES = ("hybrid_head_lm_amd/csrc/step.hip", "hybrid_head_lm_amd/csrc/hm_common.h")
+LINEAR_SOURCES = ("hybrid_head_lm_amd/csrc/linear_w4.hip", "hybrid_head_lm_amd/csrc/linear_dev.h",
+                  "hybrid_head_lm_amd/csrc/linear.hip", "hybrid_head_lm_amd/csrc/hm_common.h")
 PEAK_VALU_LANE_OPS = 256 * 64 * 2.4e9   # non-packed fp32 VALU: 64 lanes/clk/CU
 # single-pass VALU work of the SSM branch per token-channel: per state the decay
 # product, exp, h product, input term, output term (4 VALU + 1 transcendental);
@@ -273,6 +277,18 @@ def block_matmul_flops(shape, producer: bool = True) -> float:
     return 2.0 * R * macs
 
 
+def block_in_proj_operands(shape):
+    """The in-projection of a producer block at ``shape``: x [B*T, d] and the weight with
+    rows Q, K, V, x, z (device generator), and the segment widths."""
+    import torch
+    from workloads import block_inputs_torch
+    dev = torch.device("cuda")
+    t = block_inputs_torch(shape, 0, 0, True, dev, hidden=True)
+    x = t["hidden"].reshape(-1, shape.d_model).contiguous()
+    kvw = shape.Hkv * shape.Dh
+    return x, t["w_in"], [shape.Hq * shape.Dh, kvw, kvw, shape.Di, shape.Di]
+
+
 def run_blocks(shape, hm, n_layers, steps, warmup):
     """Whole blocks (norm, projections, mixer, norm, FFN) chained over one
     hidden-state tensor; weights from the device generator.  Returns ms per
@@ -301,8 +317,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="skip the global-prefill and stack lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true",
-                    help="only a 256 MiB device copy (calibration) and the attention kernel "
-                         "of the step, for rocprofv3 --pmc runs; prints no JSON")
+                    help="only a 256 MiB device copy (calibration) and the kernels whose HBM "
+                         "counters profiles/ holds, for rocprofv3 --pmc runs; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the mixer core runs on a single MI355X here "
@@ -342,9 +358,15 @@ def main():
         for _ in range(3):
             pa.run()
             pb.run()
+        del pa, pb, d
+        x, w, segs = block_in_proj_operands(BLOCK_STACK)
+        outs = [torch.empty((x.shape[0], c), dtype=torch.bfloat16, device="cuda") for c in segs]
+        for _ in range(3):
+            hm.linear(x, w, seg_cols=segs, outs=outs)
         torch.cuda.synchronize()
         print("counters run done: 3 copies of", COPY_BYTES, "bytes, then 3 each of the "
-              "attention launch, the SSM branch, the fused layer and the decode pair")
+              "attention launch, the SSM branch, the fused layer, the decode pair and the "
+              "block-stack in-projection")
         return
 
     # the step: one mixer layer (both branches on one stream, kernels in order)
@@ -574,6 +596,12 @@ def main():
                            "inputs": "torch Philox generator on the device (same distributions)"}
         torch.cuda.empty_cache()
         kms, kl, kfl_mm, kfl_at = run_blocks(BLOCK_STACK, hm, BLOCK_STACK.layers, 3, 1)
+        # the block stack's dominant kernel: a producer block's in-projection on its own
+        gx, gw, gsegs = block_in_proj_operands(BLOCK_STACK)
+        gouts = [torch.empty((gx.shape[0], c), dtype=torch.bfloat16, device="cuda") for c in gsegs]
+        gms = timed(lambda: hm.linear(gx, gw, seg_cols=gsegs, outs=gouts), 10, 2)
+        gfl = 2.0 * gx.shape[0] * gw.shape[0] * gx.shape[1]
+        del gx, gw, gouts
         result["block_stack"] = {
             "workload": BLOCK_STACK.name + " (32 whole blocks, width 1600, FFN 5504)",
             "layers": kl, "ms_per_stack": kms,
@@ -581,6 +609,13 @@ def main():
             "tokens_per_s": BLOCK_STACK.B * BLOCK_STACK.T / (kms * 1e-3),
             "tflops": (kfl_mm + kfl_at) / (kms * 1e-3) / 1e12,
             "frac_mfma": (kfl_mm + kfl_at) / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "roofline": {"bound": "mfma", "kernel": "linear_bf16_w4",
+                         "launch": "a producer block's in-projection, 33024 x 1600 -> 5440",
+                         "achieved": gfl / (gms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": gfl / (gms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "algorithmic_flop_per_launch": gfl, "ms_per_launch": gms,
+                         "traffic": traffic_from_profile(
+                             LINEAR_SOURCES, "linear_bf16_w4.block-stack32-in-proj.pmc.txt")},
             "inputs": "torch Philox generator on the device (same distributions)"}
         torch.cuda.empty_cache()
 
