@@ -128,6 +128,16 @@ def test_block_consumer_small():
     assert_close(got - h_in, ref["hidden"] - h_in, "bf16", "block increment")
 
 
+def test_block_tiny_rows():
+    """Degenerate sizes: 3 rows (1 meta + 2 tokens) per sequence, window 1
+    (each token sees itself and the meta row), widths of one tile."""
+    shape = with_(SMALL, B=2, M=1, N=2, Hq=2, Hkv=1, Di=128, W=1, d_model=64, d_ffn=64)
+    inp, h_in, got = _block_case(shape, 9, True, shape.W)
+    ref = _oracle_block(shape, inp, h_in, shape.W)
+    assert_close(got, ref["hidden"], "bf16", "hidden")
+    assert_close(got - h_in, ref["hidden"] - h_in, "bf16", "block increment")
+
+
 def test_block_swa_full_size():
     """One whole block at the model card's widths (1600, FFN 5504) over the
     swa-prefill rows (1 x (128 + 2048)), every element against the oracle."""
