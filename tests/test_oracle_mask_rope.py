@@ -123,3 +123,14 @@ def test_rope_identity_norm_and_relative_position():
         return qa @ ka
     assert abs(dot(10, 3) - dot(1010, 1003)) < 1e-9
     assert abs(dot(16511, 16500) - dot(11, 0)) < 1e-9
+
+
+def test_rope_hand_worked_fixture():
+    """tests/golden/rope_handworked.json: the pairing (d, d + Dh/2) and both
+    frequencies, derived by hand."""
+    import json
+    import os
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rope_handworked.json")))
+    x = np.array(fx["x"])[None, None, None]
+    got = oracle.rope(x, [fx["position"]], fx["base"])[0, 0, 0]
+    np.testing.assert_allclose(got, fx["out"], rtol=0, atol=1e-15)
