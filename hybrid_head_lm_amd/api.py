@@ -272,13 +272,6 @@ class BlockPlan:
         a.workspace, a.workspace_bytes = self.ws.data_ptr(), self.ws.numel()
         self.args, self.w, self.hidden = a, w, hidden
 
-    @staticmethod
-    def workspace_bytes(**kw) -> int:
-        a = BlockArgs()
-        for k, v in kw.items():
-            setattr(a, k, v)
-        return lib.hm_block_prefill_workspace(ctypes.byref(a))
-
     def run(self, stream=None):
         s = _stream() if stream is None else ctypes.c_void_p(stream.cuda_stream)
         _check(lib.hm_block_prefill(ctypes.byref(self.args), s))

@@ -29,6 +29,8 @@ size_t rows_bytes(long long rows, int width) {
   return hm::align_up((size_t)rows * (size_t)width * 2, 256);
 }
 
+// The mixer's arguments inside the block; with ws == nullptr only the fields
+// that size its workspace (shapes, dtype, kv) are set.
 hm_prefill_args mixer_args(const hm_block_args* a, const BlockLayout& L, char* ws) {
   hm_prefill_args p{};
   p.B = a->B;
@@ -46,6 +48,10 @@ hm_prefill_args mixer_args(const hm_block_args* a, const BlockLayout& L, char* w
   p.scale = a->scale;
   p.eps = a->eps;
   p.dtype = a->dtype;
+  p.kv = a->kv;
+  p.kv_bytes = a->kv_bytes;
+  p.kv_reuse = a->kv_reuse;
+  if (ws == nullptr) return p;
   p.q = ws + L.q;
   p.k = ws + L.k;
   p.v = ws + L.v;
@@ -63,9 +69,6 @@ hm_prefill_args mixer_args(const hm_block_args* a, const BlockLayout& L, char* w
   p.ya = ws + L.ya;
   p.ys = ws + L.ys;
   p.out = ws + L.mo;
-  p.kv = a->kv;
-  p.kv_bytes = a->kv_bytes;
-  p.kv_reuse = a->kv_reuse;
   p.workspace = ws + L.mix;
   p.workspace_bytes = L.total > L.mix ? L.total - L.mix : 0;
   return p;
