@@ -3,8 +3,8 @@
 // Hymba block): one workgroup of 4 waves per 256 x 256 output tile, each wave
 // owning a 128 x 128 quarter as 8 x 8 blocks of v_mfma_f32_16x16x32_bf16 with
 // its 256 accumulators in AGPRs (this file is compiled without the VGPR-only
-// MFMA form).  Per 32 of K a wave reads 16 operand fragments for 64 MFMAs,
-// a quarter of an MFMA's operand bytes in the 8-wave layout.
+// MFMA form).  Per 32 of K a wave reads 16 operand fragments (16 KB) for 64
+// MFMAs, half the LDS operand bytes per flop of the 128 x 128 kernel.
 // 64-wide K steps go HBM -> LDS with global_load_lds through two 64 KB
 // stages (one workgroup per CU); LDS rows are 128 bytes with the 16-byte chunk
 // c of row r in slot c ^ ((r >> 1) & 7), so the 16 lanes of an operand read
