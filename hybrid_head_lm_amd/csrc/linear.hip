@@ -124,34 +124,7 @@ __global__ __launch_bounds__(256) void linear_bf16(const bf16_t* __restrict__ x,
     const int row = m0 + sr, col = n0 + 8 * c;
     if (row >= M || col >= N) continue;
     const float* sp8 = stg + sr * 128 + ((8 * c) ^ (((sr >> 2) & 1) << 5));
-    const float4 v0 = *(const float4*)sp8, v1 = *(const float4*)(sp8 + 4);
-    float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    const SegPick sp = pick_segment(out, col);
-    const int cn = col - sp.c0;
-    if (sp.bias) {
-      const float4 b0 = *(const float4*)(sp.bias + cn), b1 = *(const float4*)(sp.bias + cn + 4);
-      v[0] += b0.x; v[1] += b0.y; v[2] += b0.z; v[3] += b0.w;
-      v[4] += b1.x; v[5] += b1.y; v[6] += b1.z; v[7] += b1.w;
-    }
-    if (sp.act != HM_ACT_NONE)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = lin_act(v[k], sp.act);
-    const size_t e = (size_t)row * sp.ld + cn;
-    if (sp.res) {
-      const uint4 rr = *(const uint4*)(sp.res + e);
-      const uint32_t rw[4] = {rr.x, rr.y, rr.z, rr.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[2 * k] += __uint_as_float(rw[k] << 16);
-        v[2 * k + 1] += __uint_as_float(rw[k] & 0xffff0000u);
-      }
-    }
-    uint4 o;
-    o.x = pack_bf16x2(v[0], v[1]);
-    o.y = pack_bf16x2(v[2], v[3]);
-    o.z = pack_bf16x2(v[4], v[5]);
-    o.w = pack_bf16x2(v[6], v[7]);
-    *(uint4*)(sp.dst + e) = o;
+    store_chunk8(out, row, col, *(const float4*)sp8, *(const float4*)(sp8 + 4));
   }
 }
 

@@ -45,6 +45,41 @@ HM_DEV float lin_act(float v, int act) {
   return v;
 }
 
+// The epilogue of one 16-byte output chunk: columns col .. col + 7 of `row`
+// (one segment, as segment widths are multiples of 16), v = the float32
+// products read back from the staging tile: + bias, activation, + residual,
+// rounded to bf16 and stored with one 16-byte store.
+HM_DEV void store_chunk8(const LinOut& out, int row, int col, const float4& v0,
+                         const float4& v1) {
+  float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  const SegPick sp = pick_segment(out, col);
+  const int cn = col - sp.c0;
+  if (sp.bias) {
+    const float4 b0 = *(const float4*)(sp.bias + cn), b1 = *(const float4*)(sp.bias + cn + 4);
+    v[0] += b0.x; v[1] += b0.y; v[2] += b0.z; v[3] += b0.w;
+    v[4] += b1.x; v[5] += b1.y; v[6] += b1.z; v[7] += b1.w;
+  }
+  if (sp.act != HM_ACT_NONE)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = lin_act(v[k], sp.act);
+  const size_t e = (size_t)row * sp.ld + cn;
+  if (sp.res) {
+    const uint4 rr = *(const uint4*)(sp.res + e);
+    const uint32_t rw[4] = {rr.x, rr.y, rr.z, rr.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] += __uint_as_float(rw[k] << 16);
+      v[2 * k + 1] += __uint_as_float(rw[k] & 0xffff0000u);
+    }
+  }
+  uint4 o;
+  o.x = pack_bf16x2(v[0], v[1]);
+  o.y = pack_bf16x2(v[2], v[3]);
+  o.z = pack_bf16x2(v[4], v[5]);
+  o.w = pack_bf16x2(v[6], v[7]);
+  *(uint4*)(sp.dst + e) = o;
+}
+
 // 256 x 256 tiles, 4 waves (linear_w4.hip).  Arguments validated by the caller.
 void launch_w4(const bf16_t* x, const bf16_t* w, int M, int N, int K, const LinOut& out,
                hipStream_t st);
