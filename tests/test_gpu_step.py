@@ -194,3 +194,35 @@ def test_decode_pair_bf16_ragged_global():
 def test_decode_pair_f32_ragged(Dh):
     shape = with_(TINY, B=3, n_prev=40, cache_slots=16, Dh=Dh, Di=2 * Dh)
     _check_ragged(shape, [0, 15, 40], 33)
+
+
+@pytest.mark.parametrize("n_prev,W", [(150, 64), (40, 0)])
+def test_prefill_states_feed_the_decode_step(n_prev, W):
+    """The SSM-branch states a GPU prefill returns (conv_state_out, h_out) drive
+    a GPU decode step for the next token: its output equals the last row of an
+    oracle prefill over one more row.  The cache comes from the oracle."""
+    from workloads import SWA_PREFILL, bf16_round, prefill_inputs
+    shape = with_(SWA_PREFILL, B=2, M=8, N=n_prev + 1, Hq=4, Hkv=2, Di=256, W=W)
+    M, T = shape.M, shape.M + n_prev            # prefill rows; the decode token is row T
+    full = prefill_inputs(shape, 21)
+    rows = ("q", "k", "v", "x", "delta", "Bm", "Cm", "z")
+    pre = {k: (np.ascontiguousarray(full[k][:, :T]) if k in rows else full[k]) for k in full}
+    t = up_inputs(pre, "bf16")
+    plan = hm.PrefillPlan(t, M, W, rope_base=shape.rope_base, eps=shape.eps, want_states=True)
+    plan.run()
+    slots = W if W > 0 else n_prev + 1
+    kc, vc = oracle.build_cache(full["k"], full["v"], M, n_prev, W, slots, shape.rope_base, fill=0.0)
+    step = {"q": full["q"][:, T], "k_new": full["k"][:, T], "v_new": full["v"][:, T]}
+    for k in ("x", "delta", "Bm", "Cm", "z"):
+        step[k] = full[k][:, T]
+    step = up_inputs(step, "bf16")
+    for k in ("A", "D", "conv_w", "conv_b", "beta_a", "beta_s"):
+        step[k] = t[k]
+    step["conv_state"], step["ssm_state"] = plan.conv_state, plan.h     # GPU prefill -> decode
+    kcd = up_inputs({"k_cache": bf16_round(kc)}, "bf16")["k_cache"]
+    vcd = up_inputs({"v_cache": bf16_round(vc)}, "bf16")["v_cache"]
+    sp = hm.StepPlan(step, kcd, vcd, n_prev, M, W, rope_base=shape.rope_base, eps=shape.eps)
+    sp.run()
+    torch.cuda.synchronize()
+    ref = oracle.mixer_prefill(full, M, W, shape.rope_base, shape.eps)["out"][:, T]
+    assert_close(down(sp.out), ref, "bf16", "decode after prefill")
