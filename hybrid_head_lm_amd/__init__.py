@@ -33,6 +33,7 @@ EXPORTS = (
     "hm_block_prefill", "hm_block_prefill_workspace",
     "hm_mixer_step", "hm_mixer_step_workspace",
     "hm_debug_attn_mask", "hm_debug_tile_plan", "hm_debug_attn_tiles", "hm_debug_cache_slot",
+    "hm_debug_step_positions",
 )
 
 
@@ -66,8 +67,8 @@ class StepArgs(ctypes.Structure):
         ("n_prev", _ll), ("rope_base", _f), ("scale", _f), ("eps", _f), ("dtype", _i),
     ] + [(n, _vp) for n in ("q", "k_new", "v_new", "k_cache", "v_cache", "x", "delta", "Bm", "Cm",
                             "z", "A", "D", "conv_w", "conv_b", "conv_state", "ssm_state",
-                            "beta_a", "beta_s", "out", "ya_out", "ys_out", "workspace")] + [
-        ("workspace_bytes", _sz), ("n_prev_seq", _vp)]
+                            "beta_a", "beta_s", "out", "workspace")] + [
+        ("workspace_bytes", _sz), ("ya_out", _vp), ("ys_out", _vp), ("n_prev_seq", _vp)]
 
 
 class LinearEpilogue(ctypes.Structure):
@@ -126,11 +127,12 @@ def _load():
     lib.hm_mixer_step_workspace.argtypes = [ctypes.POINTER(StepArgs)]
     lib.hm_mixer_step_workspace.restype = _sz
     lib.hm_debug_attn_mask.argtypes = [_i, _i, _i, _vp, _vp]
-    lib.hm_debug_tile_plan.argtypes = [_i, _i, _i, _i, _i, _vp, _ll, _vp]
+    lib.hm_debug_tile_plan.argtypes = [_i, _i, _i, _i, _i, _vp, _i, _vp]
     lib.hm_debug_attn_tiles.argtypes = [ctypes.POINTER(_i)] * 3
     lib.hm_debug_attn_tiles.restype = None
     lib.hm_debug_cache_slot.argtypes = [_ll, _i, _i]
     lib.hm_debug_cache_slot.restype = _ll
+    lib.hm_debug_step_positions.argtypes = [_i, _ll, _vp, _i, _i, _vp, _vp]
     return lib
 
 

@@ -18,7 +18,7 @@ __all__ = [
     "swa_meta_attn", "attn_kv_bytes", "attn_kv_prepare", "attn_with_kv", "causal_conv1d", "selective_scan", "conv_selective_scan",
     "branch_norm_mean", "linear", "rms_norm", "BlockPlan", "mixer_prefill", "PrefillPlan", "mixer_step", "StepPlan",
     "debug_attn_mask", "debug_tile_plan", "debug_attn_tiles", "debug_cache_slot",
-    "dtype_code",
+    "debug_step_positions", "dtype_code",
 ]
 
 
@@ -449,3 +449,16 @@ def debug_attn_tiles():
 
 def debug_cache_slot(n_prev: int, n_meta: int, window: int) -> int:
     return lib.hm_debug_cache_slot(n_prev, n_meta, window)
+
+
+def debug_step_positions(B: int, n_prev: int, n_meta: int, window: int, n_prev_seq=None,
+                         device="cuda"):
+    """[B, 3] int64 (slot, visible rows, position) per sequence, from the decode
+    kernels' own device function."""
+    _dev(n_prev_seq)
+    if n_prev_seq is not None and (n_prev_seq.dtype != torch.int32 or n_prev_seq.numel() != B):
+        raise TypeError("n_prev_seq must be an int32 tensor with one entry per sequence")
+    out = torch.empty((B, 3), dtype=torch.int64, device=device)
+    _check(lib.hm_debug_step_positions(B, n_prev, _p(n_prev_seq), n_meta, window, _p(out),
+                                       _stream()))
+    return out

@@ -160,9 +160,4 @@ hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream) {
   return hm::mixer_prefill_impl(a, (hipStream_t)stream, false);
 }
 
-long long hm_debug_cache_slot(long long n_prev, int n_meta, int window) {
-  if (n_prev < 0) return -1;
-  return (long long)n_meta + (window > 0 ? n_prev % window : n_prev);
-}
-
 }  // extern "C"

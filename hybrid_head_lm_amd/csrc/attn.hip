@@ -340,12 +340,13 @@ hm_status hm_debug_attn_mask(int T, int n_meta, int window, unsigned char* out_d
 }
 
 hm_status hm_debug_tile_plan(int T, int n_meta, int window, int bm, int bn, int* out_dev,
-                             long long cap, void* stream) {
+                             int cap, void* stream) {
   HM_REQUIRE(out_dev != nullptr, HM_ERR_INVALID, "out_dev is NULL");
   HM_REQUIRE(T > 0 && n_meta >= 0 && n_meta <= T && bm > 0 && bn > 0, HM_ERR_INVALID,
              "need T > 0, 0 <= n_meta <= T, bm > 0, bn > 0");
   const long long nq = (T + bm - 1) / bm, nk = (T + bn - 1) / bn;
-  HM_REQUIRE(cap >= nq * nk, HM_ERR_INVALID, "out_dev holds fewer than ceil(T/bm)*ceil(T/bn) ints");
+  HM_REQUIRE((long long)cap >= nq * nk, HM_ERR_INVALID,
+             "out_dev holds fewer than ceil(T/bm)*ceil(T/bn) ints");
   hipLaunchKernelGGL(debug_tile_kernel, dim3((unsigned)((nq + 63) / 64)), dim3(64), 0,
                      (hipStream_t)stream, T, n_meta, window, bm, bn, out_dev);
   return hm::check_launch("debug_tile_kernel");

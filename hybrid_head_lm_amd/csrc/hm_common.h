@@ -112,6 +112,33 @@ HM_HD KvRanges hm_kv_ranges(int i0, int i1, int M, int W, int bn) {
   return r;
 }
 
+// ----------------------------------------------------------------- decode positions
+// The decode token of sequence b follows n_prev earlier tokens: it sits at
+// position n_meta + n_prev, its cache slot is n_meta + (n_prev mod window)
+// (window <= 0: n_meta + n_prev) and the cache rows 0 .. L-1 with
+// L = n_meta + min(n_prev + 1, window) are visible (all n_meta + n_prev + 1 for
+// window <= 0).  Either every sequence is at n_prev_max, or nps holds one
+// n_prev per sequence, clamped to [0, n_prev_max].  Used by the decode kernels
+// and, on the host, by the slot export.
+struct SeqPos {
+  const int* nps;
+  int n_meta, window;
+  long long n_prev_max;
+};
+
+HM_HD void seq_pos(const SeqPos& sp, int b, int* L, int* slot, long long* pos) {
+  long long np = sp.n_prev_max;
+  if (sp.nps) {
+    np = (long long)sp.nps[b];
+    np = np < 0 ? 0 : (np > sp.n_prev_max ? sp.n_prev_max : np);
+  }
+  const long long nv = sp.window > 0 ? (np + 1 < sp.window ? np + 1 : (long long)sp.window)
+                                     : np + 1;
+  *L = (int)(sp.n_meta + nv);
+  *slot = (int)(sp.n_meta + (sp.window > 0 ? np % sp.window : np));
+  *pos = sp.n_meta + np;
+}
+
 // ----------------------------------------------------------------- host side
 namespace hm {
 

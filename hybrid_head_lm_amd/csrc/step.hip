@@ -184,28 +184,6 @@ HM_DEV float ssm_step_one(int b, int c, int Di, const Tact* __restrict__ x,
   return ((y4[0] + y4[1]) + (y4[2] + y4[3])) * siluf_(ldx(z + idx));
 }
 
-// ---------------------------------------------------------------- per-sequence positions
-// The token of sequence b follows n_prev earlier tokens: it sits at position
-// n_meta + n_prev, its cache slot is n_meta + (n_prev mod window) (window <= 0:
-// n_meta + n_prev) and the rows 0 .. L-1 with L = n_meta + min(n_prev + 1,
-// window) are visible (all n_prev + 1 for window <= 0).  Either every sequence
-// is at n_prev_max, or nps holds one n_prev per sequence (clamped to
-// [0, n_prev_max], which the host validated against the cache size).
-struct SeqPos {
-  const int* nps;
-  int n_meta, window;
-  long long n_prev_max;
-};
-
-HM_DEV void seq_pos(const SeqPos& sp, int b, int* L, int* slot, long long* pos) {
-  long long np = sp.n_prev_max;
-  if (sp.nps) np = min(max((long long)sp.nps[b], 0ll), sp.n_prev_max);
-  const long long nv = sp.window > 0 ? min(np + 1, (long long)sp.window) : np + 1;
-  *L = (int)(sp.n_meta + nv);
-  *slot = (int)(sp.n_meta + (sp.window > 0 ? np % sp.window : np));
-  *pos = sp.n_meta + np;
-}
-
 // ---------------------------------------------------------------- bf16 attention + SSM step
 // LDS tiles of 64 cache rows x 128 bytes (K or V); the 16-byte chunk c of row r
 // sits in slot c ^ ((r >> 1) & 7), so that 16 lanes reading one chunk of 16
@@ -601,6 +579,19 @@ __global__ __launch_bounds__(256) void step_ssm_kv(
   v_cache[off + d + half] = vs[d + half];
 }
 
+// One thread per sequence: the positions the decode kernels use (slot,
+// visible rows, position), for the bit-exact index tests.
+__global__ __launch_bounds__(64) void debug_step_pos_kernel(SeqPos sp, int B, long long* out) {
+  const int b = blockIdx.x * 64 + threadIdx.x;
+  if (b >= B) return;
+  int L, slot;
+  long long pos;
+  seq_pos(sp, b, &L, &slot, &pos);
+  out[3 * (size_t)b + 0] = slot;
+  out[3 * (size_t)b + 1] = L;
+  out[3 * (size_t)b + 2] = pos;
+}
+
 struct StepGeom {
   int L, n_split, tiles_per_split, grp;
   size_t ys_stride, part_b_stride;            // floats per sequence
@@ -622,7 +613,11 @@ StepGeom step_geom(const hm_step_args* a) {
   if (a->dtype == HM_BF16) {
     const int nt = (s.L + 63) / 64;
     const long long pairs = (long long)a->B * a->Hkv;
-    const int want = (int)std::max(1LL, std::min<long long>(nt, (kDecBlocks + pairs - 1) / pairs));
+    // the combine holds (max, sum) of every (query head, split) in LDS: at
+    // most kCombMaxW of them, so long caches get longer splits
+    const long long cap = std::max(1, kCombMaxW / std::max(1, a->Hq));
+    const int want = (int)std::max(
+        1LL, std::min<long long>(std::min<long long>(nt, cap), (kDecBlocks + pairs - 1) / pairs));
     s.tiles_per_split = (nt + want - 1) / want;
     s.n_split = (nt + s.tiles_per_split - 1) / s.tiles_per_split;
   }
@@ -642,6 +637,25 @@ size_t hm_mixer_step_workspace(const hm_step_args* a) {
     return 0;
   const StepGeom s = step_geom(a);
   return s.ys_bytes + s.part_bytes;
+}
+
+long long hm_debug_cache_slot(long long n_prev, int n_meta, int window) {
+  if (n_prev < 0) return -1;
+  int L, slot;
+  long long pos;
+  seq_pos(SeqPos{nullptr, n_meta, window, n_prev}, 0, &L, &slot, &pos);
+  return slot;
+}
+
+hm_status hm_debug_step_positions(int B, long long n_prev, const int* n_prev_seq, int n_meta,
+                                  int window, long long* out_dev, void* stream) {
+  HM_REQUIRE(out_dev != nullptr, HM_ERR_INVALID, "out_dev is NULL");
+  HM_REQUIRE(B > 0 && n_prev >= 0 && n_meta >= 0, HM_ERR_INVALID,
+             "need B > 0, n_prev >= 0 and n_meta >= 0");
+  HM_REQUIRE(n_meta + n_prev < (1LL << 31) - 1, HM_ERR_UNSUPPORTED, "positions must fit int32");
+  hipLaunchKernelGGL(debug_step_pos_kernel, dim3((B + 63) / 64), dim3(64), 0,
+                     (hipStream_t)stream, SeqPos{n_prev_seq, n_meta, window, n_prev}, B, out_dev);
+  return hm::check_launch("debug_step_pos_kernel");
 }
 
 hm_status hm_mixer_step(const hm_step_args* a, void* stream) {

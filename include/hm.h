@@ -354,11 +354,12 @@ typedef struct {
   const float *A, *D, *conv_w, *conv_b;    /* [Di,N], [Di], [Di,K], [Di] */
   float *conv_state, *ssm_state;           /* [B,Di,K-1], [B,Di,N]   in/out */
   const float *beta_a, *beta_s;            /* [Di] */
-  void* out;                               /* [B, Di] */
-  float *ya_out, *ys_out;                  /* optional [B, Di] */
+  void* out;                               /* [B, Di] (Di == Hq * Dh) */
   void* workspace;
   size_t workspace_bytes;
-  const int* n_prev_seq;                   /* optional [B] device int32, see below */
+  /* optional fields after the contract's prefix (NULL: unused) */
+  float *ya_out, *ys_out;                  /* [B, Di] f32 branch outputs */
+  const int* n_prev_seq;                   /* [B] device int32, see above */
 } hm_step_args;
 hm_status hm_mixer_step(const hm_step_args* a, void* stream);
 size_t hm_mixer_step_workspace(const hm_step_args* a);
@@ -373,14 +374,25 @@ size_t hm_mixer_step_workspace(const hm_step_args* a);
  *     hm_debug_attn_tiles() reports the tile sizes the bf16 kernel runs with
  *     (query rows per workgroup, per wave, and keys per tile).
  *     cap = number of int32 elements available at out_dev.
- *   hm_debug_cache_slot: host function, the decode ring slot (-1 if n_prev < 0).
+ *   hm_debug_cache_slot: the decode ring slot of a token after n_prev earlier
+ *     ones (-1 if n_prev < 0), evaluated on the host by the same
+ *     host-and-device function the decode kernels call.
+ *   hm_debug_step_positions: the decode kernels' per-sequence positions,
+ *     computed on the device by their own function: out_dev (int64 [B, 3],
+ *     device) receives for sequence b its cache slot, its number of visible
+ *     cache rows and its position, exactly as hm_mixer_step uses them for
+ *     the same n_prev, n_prev_seq (device int32 [B] or NULL), n_meta and
+ *     window (window <= 0: global).  HM_ERR_INVALID for B <= 0, n_prev < 0,
+ *     n_meta < 0 or out_dev NULL.
  * ---------------------------------------------------------------------- */
 hm_status hm_debug_attn_mask(int T, int n_meta, int window, unsigned char* out_dev,
                              void* stream);
 hm_status hm_debug_tile_plan(int T, int n_meta, int window, int bm, int bn,
-                             int* out_dev, long long cap, void* stream);
+                             int* out_dev, int cap, void* stream);
 void hm_debug_attn_tiles(int* bm_workgroup, int* bm_wave, int* bn);
 long long hm_debug_cache_slot(long long n_prev, int n_meta, int window);
+hm_status hm_debug_step_positions(int B, long long n_prev, const int* n_prev_seq,
+                                  int n_meta, int window, long long* out_dev, void* stream);
 
 #ifdef __cplusplus
 }

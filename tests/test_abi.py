@@ -44,6 +44,25 @@ def test_cache_slot_matches_oracle():
     assert hm.debug_cache_slot(-1, 1, 1) == -1
 
 
+def test_step_key_splits_fit_the_combine():
+    """A global layer's decode at one sequence and a long cache: the key splits
+    are capped so that every (query head, split) fits the combine (at most 2048
+    of them), which the workspace size shows (one partial of Dh + 2 floats
+    per split, KV head and query head of the group)."""
+    L = hm.lib
+    for n_prev in (3000, 6000, 10240, 16384):
+        a = hm.StepArgs(B=1, Hq=25, Hkv=5, Dh=64, Di=1600, N=16, K=4, n_meta=128, window=0,
+                        cache_slots=16512, n_prev=n_prev, dtype=hm.HM_BF16)
+        nb = L.hm_mixer_step_workspace(ctypes.byref(a))
+        ys = -(-1600 // 64) * 64 * 4
+        part_floats = (nb - ys) // 4
+        n_split = part_floats // (5 * 5 * 66)
+        assert 1 <= n_split and 25 * n_split <= 2048, (n_prev, n_split)
+        # and the splits cover every visible tile
+        tiles = -(-(128 + n_prev + 1) // 64)
+        assert n_split * -(-tiles // n_split) >= tiles
+
+
 def test_workspace_queries():
     L = hm.lib
     assert L.hm_swa_meta_attn_workspace(1, 2176, 5, 64, hm.HM_BF16) == 2 * 5 * 2176 * 64 * 2
@@ -180,6 +199,59 @@ def test_ctypes_structs_match_the_header(tmp_path):
         assert vals[1:1 + n] == [getattr(cls, f).offset for f, _ in cls._fields_], cname
         vals = vals[1 + n:]
     assert vals == []
+
+
+# The decode-step argument struct as the contract fixes it (field order and
+# types); the library's hm_step_args must start with exactly this prefix, so a
+# caller built against the contract passes every field where the library
+# reads it.  Optional fields may only follow workspace_bytes.
+STEP_CONTRACT = """
+typedef struct {
+  int B, Hq, Hkv, Dh, Di, N, K, n_meta, window, cache_slots; long long n_prev;
+  float rope_base, scale, eps; hm_dtype dtype;
+  const void *q, *k_new, *v_new;
+  void *k_cache, *v_cache;
+  const void *x, *delta, *Bm, *Cm, *z;
+  const float *A, *D, *conv_w, *conv_b;
+  float *conv_state, *ssm_state;
+  const float *beta_a, *beta_s;
+  void *out;
+  void *workspace; size_t workspace_bytes;
+} step_contract;
+"""
+STEP_CONTRACT_FIELDS = ("B", "Hq", "Hkv", "Dh", "Di", "N", "K", "n_meta", "window",
+                        "cache_slots", "n_prev", "rope_base", "scale", "eps", "dtype", "q",
+                        "k_new", "v_new", "k_cache", "v_cache", "x", "delta", "Bm", "Cm", "z",
+                        "A", "D", "conv_w", "conv_b", "conv_state", "ssm_state", "beta_a",
+                        "beta_s", "out", "workspace", "workspace_bytes")
+
+
+def test_step_args_start_with_the_contract_prefix(tmp_path):
+    import shutil
+    import subprocess
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    src = tmp_path / "contract.cpp"
+    lines = ['#include "hm.h"', "#include <cstdio>", "#include <cstddef>", STEP_CONTRACT,
+             "int main() {"]
+    for f in STEP_CONTRACT_FIELDS:
+        lines.append(f'printf("%zu %zu\\n", offsetof(step_contract, {f}), '
+                     f'offsetof(hm_step_args, {f}));')
+    lines += ['printf("%zu %zu\\n", sizeof(step_contract), offsetof(hm_step_args, ya_out));',
+              "return 0; }"]
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "contract"
+    subprocess.run([cxx, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    rows = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    pairs = [tuple(int(v) for v in r.split()) for r in rows if r.strip()]
+    assert len(pairs) == len(STEP_CONTRACT_FIELDS) + 1
+    for f, (want, got) in zip(STEP_CONTRACT_FIELDS, pairs):
+        assert want == got, f"hm_step_args.{f} at offset {got}, the contract puts it at {want}"
+        assert getattr(hm.StepArgs, f).offset == want, f
+    # the optional fields start where the contract's struct ends
+    assert pairs[-1][0] <= pairs[-1][1]
 
 
 def test_empty_extents_are_rejected():

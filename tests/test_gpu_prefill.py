@@ -101,6 +101,36 @@ def test_attention_bf16_global_full_size_sampled_rows():
     assert_close(got, ref, "bf16", "attention global full size")
 
 
+def test_global_layer_full_size():
+    """The whole global-attention layer at full size (B=4, 128 + 8192 rows) in
+    the launch configuration the benchmark times (the fused one-stream
+    sequence): attention and fused output on rows sampled across query and
+    key tiles, the end of the meta prefix and the last rows; the SSM branch on
+    every row and its final conv and SSM states against a full sequential
+    oracle scan."""
+    shape = GLOBAL_PREFILL
+    inp = prefill_inputs(shape, 4)
+    t = up_inputs(inp, "bf16")
+    plan = hm.PrefillPlan(t, shape.M, shape.W, rope_base=shape.rope_base, eps=shape.eps)
+    plan.run()
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set([0, 1, 63, 64, 127, 128, 129, 191, 192, 255, 256, 2047, 2048,
+                                4160, 6000, 8191, 8255, 8256, 8318, 8319] +
+                               list(np.random.default_rng(1).integers(0, shape.T, 12)))))
+    ya_ref = oracle.attention(inp["q"], inp["k"], inp["v"], shape.M, shape.W, shape.rope_base,
+                              rows=rows).reshape(shape.B, len(rows), shape.Di)
+    assert_close(down(plan.ya)[:, rows], ya_ref, "bf16", "global layer attention rows")
+    xc, cs_ref = oracle.causal_conv1d(inp["x"], inp["conv_w"], inp["conv_b"], None, True)
+    ys_ref, h_ref = oracle.selective_scan(xc, inp["delta"], inp["A"], inp["Bm"], inp["Cm"],
+                                          inp["D"], inp["z"])
+    assert_close(down(plan.ys), ys_ref, "bf16", "global layer ssm branch, every row")
+    assert_close(down(plan.h), h_ref, "bf16", "global layer final ssm state")
+    assert np.array_equal(down(plan.conv_state), cs_ref), "global layer final conv state"
+    out_ref = oracle.branch_norm_mean(ya_ref, ys_ref[:, rows], inp["beta_a"], inp["beta_s"],
+                                      shape.eps)
+    assert_close(down(plan.out)[:, rows], out_ref, "bf16", "global layer out rows")
+
+
 # ------------------------------------------------------------------ conv / scan / norm
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("T", [1, 2, 5, 64, 200])

@@ -3,8 +3,8 @@
 Adjacent sliding-window layers share the producer's prepared K/V; layers 0, 15
 and 31 are global.  The whole stack runs on the GPU; the oracle then checks
 sampled rows of selected layers (global, producer, consumer, unpaired): the
-attention rows directly, the SSM branch with a full sequential scan, and the
-fused output of those rows.
+attention rows directly, the SSM branch with a full sequential scan (and the
+final conv and SSM states), and the fused output of those rows.
 """
 import numpy as np
 import pytest
@@ -32,8 +32,9 @@ def test_stack_full_size_sampled():
     stack = hm.StackPlan(layers, roles, shape.M, shape.rope_base, shape.eps, keep_outputs=True)
     stack.run()
     torch.cuda.synchronize()
-    rows = np.array([0, 127, 128, 1151, 1152, 5000, 9999, 16511])
-    for layer in (0, 1, 2, 30):
+    rows = np.array([0, 127, 128, 1151, 1152, 5000, 9999, 16383, 16384, 16511])
+    # global first, producer, consumer, global middle, unpaired window, global last
+    for layer in (0, 1, 2, 15, 30, 31):
         window, src = roles[layer]
         t = layers[layer]
         h = {k: down(v) for k, v in t.items() if k not in ("k", "v")}
@@ -42,11 +43,12 @@ def test_stack_full_size_sampled():
                                   rows=rows).reshape(shape.B, len(rows), shape.Di)
         p = stack.plans[layer]
         assert_close(down(p.ya)[:, rows], ya_ref, "bf16", f"layer {layer} attention rows")
-        xc, _ = oracle.causal_conv1d(h["x"], h["conv_w"], h["conv_b"], None, True)
+        xc, cs_ref = oracle.causal_conv1d(h["x"], h["conv_w"], h["conv_b"], None, True)
         ys_ref, h_ref = oracle.selective_scan(xc, h["delta"], h["A"], h["Bm"], h["Cm"], h["D"],
                                               h["z"])
         assert_close(down(p.ys)[:, rows], ys_ref[:, rows], "bf16", f"layer {layer} ssm rows")
         assert_close(down(p.h), h_ref, "bf16", f"layer {layer} final state")
+        assert np.array_equal(down(p.conv_state), cs_ref), f"layer {layer} conv state"
         out_ref = oracle.branch_norm_mean(ya_ref, ys_ref[:, rows], h["beta_a"], h["beta_s"],
                                           shape.eps)
         assert_close(down(p.out)[:, rows], out_ref, "bf16", f"layer {layer} out rows")

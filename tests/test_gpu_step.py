@@ -83,6 +83,40 @@ def test_decode_pair_bf16_global_long_cache():
     _check(shape, 17)
 
 
+@pytest.mark.parametrize("n_prev", [6000, 16384])
+def test_decode_pair_bf16_global_single_sequence(n_prev):
+    """One sequence through a global layer with a long cache: the most key
+    splits per (sequence, KV head), capped so that the combine holds every
+    (query head, split) pair (the stack's global layers at 16 K context)."""
+    shape = with_(DECODE_PAIR, B=1, W=0, cache_slots=16512, n_prev=n_prev, M=128)
+    _check(shape, 23)
+
+
+@pytest.mark.parametrize("B,n_prev,M,W", [(64, 2048, 128, 1024), (5, 0, 4, 16), (7, 999, 3, 0),
+                                          (130, 5000, 128, 1024)])
+def test_step_positions_bit_exact(B, n_prev, M, W):
+    """Slot, visible rows and position of every sequence, from the decode
+    kernels' own device function, against the oracle's ring slot and valid
+    slot set; uniform and ragged batches (entries past n_prev and below zero
+    clamped)."""
+    rng = np.random.default_rng(B + n_prev)
+    for ragged in (False, True):
+        nps = None
+        if ragged:
+            nps = rng.integers(-3, n_prev + 4, size=B).astype(np.int32)
+        got = hm.debug_step_positions(B, n_prev, M, W,
+                                      None if nps is None else torch.from_numpy(nps).cuda())
+        got = got.cpu().numpy()
+        for b in range(B):
+            npb = n_prev if nps is None else int(min(max(nps[b], 0), n_prev))
+            slot = oracle.cache_slot(npb, M, W)
+            valid = oracle.valid_slots(npb, M, W)
+            assert got[b, 0] == slot, (b, npb)
+            # the kernels read rows 0 .. L-1: exactly the valid slots
+            assert np.array_equal(valid, np.arange(got[b, 1])), (b, npb)
+            assert got[b, 2] == M + npb
+
+
 @pytest.mark.parametrize("n_prev", [0, 5, 15, 16, 40])
 @pytest.mark.parametrize("Dh", [16, 64])
 def test_decode_pair_f32(n_prev, Dh):

@@ -27,6 +27,31 @@ def test_mask_row_counts_closed_form(T, M, W):
     assert int(m.sum()) == int(expect.sum())
 
 
+@pytest.mark.parametrize("T,M,W", CASES)
+def test_visible_count_closed_form_and_brute_force(T, M, W):
+    # visible_count against (1) the closed form min(i+1, M+W) (i+1 without a
+    # window) and (2) row sums of the scalar predicate enumerated pair by pair
+    got = oracle.visible_count(T, M, W)
+    i = np.arange(T)
+    closed = i + 1 if W <= 0 else np.minimum(i + 1, M + W)
+    assert got.shape == (T,)
+    assert np.array_equal(got, closed)
+    brute = [sum(1 for j in range(T) if oracle.visible(r, j, M, W)) for r in range(T)]
+    assert np.array_equal(got, np.array(brute))
+
+
+def test_visible_count_planted_mistakes_fail():
+    # the closed form distinguishes the plausible mistakes: a window counted
+    # without the row itself, meta keys counted twice, or the count taken
+    # over the key axis (column sums)
+    T, M, W = 40, 4, 8
+    got = oracle.visible_count(T, M, W)
+    i = np.arange(T)
+    assert not np.array_equal(got, np.minimum(i, M + W - 1) + 1 - (i >= M + W - 1))
+    assert not np.array_equal(got, np.minimum(i + 1, M + W) + np.minimum(i + 1, M))
+    assert not np.array_equal(got, oracle.mask(T, M, W).sum(axis=0))
+
+
 @pytest.mark.parametrize("T,M", [(1, 0), (9, 3), (64, 4), (100, 0)])
 def test_window_at_least_length_is_causal(T, M):
     causal = np.tril(np.ones((T, T), dtype=bool))
