@@ -31,7 +31,8 @@ EXPORTS = (
     "hm_conv_selective_scan", "hm_branch_norm_mean", "hm_linear_bf16", "hm_linear_bf16_ex",
     "hm_rms_norm", "hm_mixer_prefill", "hm_mixer_prefill_workspace",
     "hm_block_prefill", "hm_block_prefill_workspace",
-    "hm_mixer_step", "hm_mixer_step_workspace",
+    "hm_mixer_step", "hm_mixer_step_workspace", "hm_mixer_step_noalloc",
+    "hm_mixer_step_noalloc_max_bytes",
     "hm_debug_attn_mask", "hm_debug_tile_plan", "hm_debug_attn_tiles", "hm_debug_cache_slot",
     "hm_debug_step_positions",
 )
@@ -126,6 +127,9 @@ def _load():
     lib.hm_mixer_step.argtypes = [ctypes.POINTER(StepArgs), _vp]
     lib.hm_mixer_step_workspace.argtypes = [ctypes.POINTER(StepArgs)]
     lib.hm_mixer_step_workspace.restype = _sz
+    lib.hm_mixer_step_noalloc.argtypes = [ctypes.POINTER(StepArgs), _vp]
+    lib.hm_mixer_step_noalloc_max_bytes.argtypes = []
+    lib.hm_mixer_step_noalloc_max_bytes.restype = _sz
     lib.hm_debug_attn_mask.argtypes = [_i, _i, _i, _vp, _vp]
     lib.hm_debug_tile_plan.argtypes = [_i, _i, _i, _i, _i, _vp, _i, _vp]
     lib.hm_debug_attn_tiles.argtypes = [ctypes.POINTER(_i)] * 3

@@ -19,6 +19,8 @@
 // (b, head) over all visible rows, then the same combine kernel.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
+#include <string>
 
 #include "hm_common.h"
 
@@ -658,7 +660,14 @@ hm_status hm_debug_step_positions(int B, long long n_prev, const int* n_prev_seq
   return hm::check_launch("debug_step_pos_kernel");
 }
 
-hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode step with its scratch memory given explicitly (ws, ws_bytes):
+// the caller's workspace (hm_mixer_step) or the library's static scratch
+// array (hm_mixer_step_noalloc).  a->workspace is not read here.
+hm_status mixer_step_impl(const hm_step_args* a, void* ws, size_t ws_bytes, void* stream) {
   HM_REQUIRE(a != nullptr, HM_ERR_INVALID, "args is NULL");
   HM_REQUIRE(a->B > 0 && a->Hq > 0 && a->Hkv > 0 && a->Dh > 0 && a->Di > 0, HM_ERR_INVALID,
              "B, Hq, Hkv, Dh and Di must be positive");
@@ -719,12 +728,12 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
   const size_t need = g.ys_bytes + g.part_bytes;
   HM_REQUIRE((size_t)a->Hq * g.n_split <= (size_t)kCombMaxW, HM_ERR_UNSUPPORTED,
              "too many query heads x key splits for the combine");
-  HM_REQUIRE(a->workspace != nullptr && a->workspace_bytes >= need && hm::aligned16(a->workspace),
-             HM_ERR_WORKSPACE, "workspace smaller than hm_mixer_step_workspace()");
+  HM_REQUIRE(ws != nullptr && ws_bytes >= need && hm::aligned16(ws), HM_ERR_WORKSPACE,
+             "workspace smaller than hm_mixer_step_workspace()");
 
   hipStream_t st = (hipStream_t)stream;
-  float* ys_ws = (float*)a->workspace;
-  float* part = (float*)((char*)a->workspace + g.ys_bytes);
+  float* ys_ws = (float*)ws;
+  float* part = (float*)((char*)ws + g.ys_bytes);
   const int S = a->n_meta + a->cache_slots;
   const SeqPos sp{a->n_prev_seq, a->n_meta, a->window, a->n_prev};
   const double l2b = log2((double)a->rope_base);
@@ -780,6 +789,65 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
                      g.part_b_stride, (const float*)ys_ws, g.ys_stride, a->beta_a, a->beta_s,
                      a->eps, (float*)a->out, a->ya_out, a->ys_out, a->Hq, a->Hkv, a->Dh, 1, a->Di);
   return hm::check_launch("step_combine");
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+// Scratch of hm_mixer_step_noalloc: a file-scope device array, one copy per
+// GPU, alive until the process ends.  Host code never passes `step_scratch`
+// itself (on the host it is only a stand-in for the symbol): its device
+// address is looked up once per device with hipGetSymbolAddress and that
+// address is what the kernels receive.
+constexpr size_t kStepScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char step_scratch[kStepScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchAddr {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+static ScratchAddr g_scratch[kMaxDevices];
+
+hm_status step_scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return hm::fail(HM_ERR_HIP, "hipGetDevice failed or device index >= 64");
+  ScratchAddr& s = g_scratch[dev];
+  // once per device, with that device current (the calling thread's device)
+  std::call_once(s.once, [&s]() {
+    void* p = nullptr;
+    s.err = hipGetSymbolAddress(&p, HIP_SYMBOL(step_scratch));
+    s.ptr = p;
+  });
+  if (s.err != hipSuccess || s.ptr == nullptr)
+    return hm::fail(HM_ERR_HIP, std::string("hipGetSymbolAddress(step_scratch): ") +
+                                    hipGetErrorString(s.err));
+  *out = s.ptr;
+  return HM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
+  HM_REQUIRE(a != nullptr, HM_ERR_INVALID, "args is NULL");
+  return mixer_step_impl(a, a->workspace, a->workspace_bytes, stream);
+}
+
+size_t hm_mixer_step_noalloc_max_bytes(void) { return kStepScratchBytes; }
+
+hm_status hm_mixer_step_noalloc(const hm_step_args* a, void* stream) {
+  HM_REQUIRE(a != nullptr, HM_ERR_INVALID, "args is NULL");
+  const size_t need = hm_mixer_step_workspace(a);
+  HM_REQUIRE(need <= kStepScratchBytes, HM_ERR_UNSUPPORTED,
+             "step needs " + std::to_string(need) + " bytes of scratch, more than the " +
+                 std::to_string(kStepScratchBytes) +
+                 " of the allocation-free entry point; use hm_mixer_step with a workspace");
+  void* ws = nullptr;
+  hm_status s = step_scratch_ptr(&ws);
+  if (s != HM_OK) return s;
+  return mixer_step_impl(a, ws, kStepScratchBytes, stream);
 }
 
 }  // extern "C"

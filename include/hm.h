@@ -365,6 +365,24 @@ hm_status hm_mixer_step(const hm_step_args* a, void* stream);
 size_t hm_mixer_step_workspace(const hm_step_args* a);
 
 /* ------------------------------------------------------------------------
+ * hm_mixer_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results as hm_mixer_step, with the scratch memory
+ * taken from a static device array inside the library (one per GPU, held
+ * until the process ends) instead of a->workspace, which is not read.  The
+ * caller still passes every input and output.  The call allocates nothing.
+ * Limit: hm_mixer_step_workspace(a) must not exceed
+ * hm_mixer_step_noalloc_max_bytes() (8 MiB; the 64-sequence decode pair with
+ * a 1152-row cache needs 1.3 MB), else HM_ERR_UNSUPPORTED and nothing runs.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that may overlap on one GPU (different streams without
+ * ordering, several host threads) race and must not be used; calls ordered
+ * on one stream are fine.  No part of the array needs clearing between calls.
+ * ---------------------------------------------------------------------- */
+hm_status hm_mixer_step_noalloc(const hm_step_args* a, void* stream);
+size_t hm_mixer_step_noalloc_max_bytes(void);
+
+/* ------------------------------------------------------------------------
  * Index exports, computed by the same device predicates the kernels use.
  *   hm_debug_attn_mask: out_dev[i*T + j] = 1 if row i may attend row j (u8 [T,T]).
  *   hm_debug_tile_plan: out_dev[a*nk + c] (int32 [ceil(T/bm), ceil(T/bn)]) =
