@@ -1,49 +1,42 @@
 #!/usr/bin/env python3
 """Benchmark of the Hymba hybrid-head mixer core on one MI355X.
 
-A step is one prefill pass of one mixer layer (RoPE, the meta + sliding-window
-GQA attention, the causal conv + selective scan branch, the branch norm and
-average; all kernels in order on one stream) over the sliding-window
-workload: batch 1, 128 meta + 2048 tokens, 25 query heads x 64, 5 KV heads,
-window 1024, SSM width 1600 x 16 states, bf16 inputs with float32
-accumulation, synthetic seeded inputs resident in HBM.
-`value` is prefill tokens/s per layer (B * (M + N) rows / step time).
+A step is one prefill pass of the 32-layer mixer stack (stack32-b2-t16512):
+batch 2, 128 meta + 16384 tokens, 25 query heads x 64, 5 KV heads, SSM width
+1600 x 16 states, conv width 4; layers 0, 15 and 31 global, the others a
+1024-row sliding window with adjacent window layers sharing the producer's
+prepared K/V; each layer is RoPE, the meta + window GQA attention, the causal
+conv + selective scan branch and the branch norm and average, as three
+launches on one stream; bf16 inputs with float32 accumulation, synthetic
+seeded inputs resident in HBM.  `value` = prefill tokens/s per layer
+(B * (M + N) rows * 32 layers / pass time), timed with HIP events over K
+passes during which the library also records its launch boundaries.
 
 Also reported on the same JSON line:
-  roofline      the attention kernel (the dominant one) timed on its own with
-                HIP events on its stream: algorithmic FLOPs / time vs the bf16
-                MFMA peak;
-  decode        one token for 64 sequences through an adjacent pair of layers
-                that share a 128 + 1024-row KV cache: steps/s and HBM fraction,
-                with the Infinity Cache flushed before each step (and warm);
-  global_prefill, stack
-                the global-attention layer (batch 4, 128 + 8192 tokens) and the
-                32-layer stack (batch 2, 128 + 16384 tokens, layers 0/15/31
-                global, adjacent sliding-window layers sharing prepared K/V);
-  ragged_decode the decode pair with one n_prev per sequence (warm);
-  projections   the in- and out-projections around the layer (bf16 MFMA GEMM);
-  block         one whole Hymba block (RMS norm, in-projection, step-size/B/C
-                projection, the mixer, out-projection with the skip connection,
-                RMS norm, FFN 1600 -> 5504 -> 1600 with the skip connection) over
-                the same rows at the model card's widths;
-  block_stack   32 whole blocks chained over one hidden-state tensor at the
-                stack's size (batch 2, 128 + 16384 tokens; KV shared as above);
-  cached_meta   the same layer with the meta tokens' K/V and SSM states taken
-                from a cache: only the 2048 real-token rows are computed
-                (real tokens/s, beside the full layer's real tokens/s);
-  layer_step_us single-call times of the step (median, p10, p90) after the timed
-                region, and (sclk_mhz) the shader clock the driver reports while
-                those calls run;
-  ssm_branch    the conv + scan branch on its own against HBM and against the
-                non-packed fp32 VALU rate (single-pass VALU work per
-                token-channel);
-  cpu_baseline  the float64 CPU oracle on one whole layer of the step's workload.
-HBM traffic (`traffic`) of the attention kernel, the SSM branch, the decode pair
-and the block stack's in-projection GEMM (block_stack.roofline, the block's
-dominant kernel timed on its own) comes from the committed rocprofv3 counter
-summaries in profiles/ (null
-once the kernel sources differ from those the counters were taken with);
-`--counters` is the run those summaries are taken over.
+  roofline       the step's dominant kernel, the middle launch of a window layer
+                 (attention | final scan pass), from the library's events around
+                 it in every timed pass: attention FLOPs / time against the bf16
+                 MFMA peak; the same for the three global layers (`global`);
+  stack_kernels_us  mean time of each of the three launches per layer role;
+  swa_prefill    one window layer (batch 1, 128 + 2048 rows): layer time, its
+                 launches, and the attention kernel alone;
+  cached_meta    that layer with the meta rows' K/V and SSM states cached;
+  projections    the in- and out-projections around that layer;
+  ssm_branch     the conv + scan branch alone against HBM and against the
+                 measured ALU ceiling of its instruction mix (alu_probe);
+  global_prefill the global layer (batch 4, 128 + 8192 rows);
+  decode         one token for 64 sequences through an adjacent pair of layers
+                 sharing a 128 + 1024-row KV cache: steps/s and HBM fraction with
+                 the Infinity Cache flushed before each step (and warm);
+  ragged_decode  the decode pair with one n_prev per sequence (warm);
+  block, block_stack  whole Hymba blocks (norm, projections, mixer, norm, FFN):
+                 one over the swa-prefill rows, 32 chained at the stack's size;
+  cpu_baseline   the float64 CPU oracle on a bounded sample of the stack
+                 (layers 0, 1, 2, 15, 30, 31), extrapolated, in the step's unit;
+  cpu_baseline_decode  the oracle's decode step through the pair.
+HBM traffic (`traffic`) comes from the committed rocprofv3 counter summaries in
+profiles/ (null once the kernel sources differ from those the counters were
+taken with); `--counters` is the run those summaries are taken over.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
                        [--no-cpu-baseline] [--counters]
@@ -69,6 +62,8 @@ ATTN_SOURCES = ("hybrid_head_lm_amd/csrc/attn_dev.h", "hybrid_head_lm_amd/csrc/a
 SSM_SOURCES = ("hybrid_head_lm_amd/csrc/ssm_dev.h", "hybrid_head_lm_amd/csrc/ssm.hip",
                "hybrid_head_lm_amd/csrc/hm_common.h")
 STEP_SOURCES = ("hybrid_head_lm_amd/csrc/step.hip", "hybrid_head_lm_amd/csrc/hm_common.h")
+FUSED_SOURCES = ("hybrid_head_lm_amd/csrc/fused.hip", "hybrid_head_lm_amd/csrc/attn_dev.h",
+                 "hybrid_head_lm_amd/csrc/ssm_dev.h", "hybrid_head_lm_amd/csrc/hm_common.h")
 LINEAR_SOURCES = ("hybrid_head_lm_amd/csrc/linear_w4.hip", "hybrid_head_lm_amd/csrc/linear_dev.h",
                   "hybrid_head_lm_amd/csrc/linear.hip", "hybrid_head_lm_amd/csrc/hm_common.h")
 PEAK_VALU_LANE_OPS = 256 * 64 * 2.4e9   # non-packed fp32 VALU: 64 lanes/clk/CU
@@ -214,29 +209,149 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(shape, inp, min_seconds: float = 10.0):
-    """The oracle (float64 NumPy) on whole prefill layers of the workload,
-    repeated until at least `min_seconds` of CPU work have been timed."""
-    import oracle
-    threads = None
+def blas_threads():
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
-        threads = max((d.get("num_threads") or 1) for d in info) if info else 1
+        return max((d.get("num_threads") or 1) for d in info) if info else 1
     except Exception:
-        pass
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.mixer_prefill(inp, shape.M, shape.W, shape.rope_base, shape.eps)
-        n += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
-            break
-    return {"value": n * shape.B * shape.T / dt, "unit": "tokens/s", "cores": threads or 1,
-            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(), "kind": "oracle",
-            "sample": f"{n} whole prefill layers of {shape.name} (float64 NumPy, same "
-                      f"inputs each time), {dt:.1f} s"}
+        return None
+
+
+def _host(t):
+    """A device tensor as float64 NumPy (bf16 widened exactly)."""
+    import numpy as np
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+# sampled layers of the stack: global first, producer, consumer, global
+# middle, unpaired window layer, global last
+CPU_STACK_LAYERS = (0, 1, 2, 15, 30, 31)
+CPU_QUERY_BLOCK = 512      # the oracle attention's own query-block size
+CPU_SCAN_ROWS = 1024       # rows of the sequential scan timed per layer
+
+
+def cpu_baseline_stack(shape, layers, roles):
+    """The oracle (float64 NumPy, as it stands) on a bounded sample of the
+    32-layer stack, extrapolated to the whole stack.
+
+    Per sampled layer: the oracle attention over one 512-row query block (its
+    own block size: it scores every key of a row and masks, so each block
+    costs the same) and, timed separately, the rotation of all K rows it does
+    once per call; the conv + selective scan over the first 1024 rows (the
+    scan is sequential, linear in the rows); the branch norm-and-average of
+    those rows.  Layer estimate = K rotation + (T / 512) blocks + (T / 1024) x
+    (conv + scan + norm).  Stack estimate = 3 x mean(global layers) + 29 x
+    mean(window layers).  Inputs are the stack's own device tensors copied to
+    the host (the same bytes the GPU read)."""
+    import numpy as np
+    import oracle
+    T, B = shape.T, shape.B
+    n_blocks = -(-T // CPU_QUERY_BLOCK)
+    qrows = np.arange(T // 2, T // 2 + CPU_QUERY_BLOCK)
+    per_role = {"global": [], "window": []}
+    t_all0 = time.perf_counter()
+    for layer in CPU_STACK_LAYERS:
+        window, src = roles[layer]
+        t = layers[layer]
+        q = _host(t["q"])
+        k, v = _host(layers[src]["k"]), _host(layers[src]["v"])
+        S = CPU_SCAN_ROWS
+        part = {n: _host(t[n][:, :S]) for n in ("x", "delta", "Bm", "Cm", "z")}
+        prm = {n: _host(t[n]) for n in ("A", "D", "conv_w", "conv_b", "beta_a", "beta_s")}
+        # the K rotation of one attention call
+        t0 = time.perf_counter()
+        oracle.rope(k, np.arange(T), shape.rope_base)
+        t_rope = time.perf_counter() - t0
+        # one query block: the call rotates all of K once, so subtract that
+        t0 = time.perf_counter()
+        ya = oracle.attention(q, k, v, shape.M, window, shape.rope_base, rows=qrows)
+        t_blk = time.perf_counter() - t0 - t_rope
+        t0 = time.perf_counter()
+        xc, _ = oracle.causal_conv1d(part["x"], prm["conv_w"], prm["conv_b"], None, True)
+        ys, _ = oracle.selective_scan(xc, part["delta"], prm["A"], part["Bm"], part["Cm"],
+                                      prm["D"], part["z"])
+        t_ssm = time.perf_counter() - t0
+        nr = min(S, len(qrows))
+        t0 = time.perf_counter()
+        oracle.branch_norm_mean(ya.reshape(B, len(qrows), -1)[:, :nr], ys[:, :nr],
+                                prm["beta_a"], prm["beta_s"], shape.eps)
+        t_norm = time.perf_counter() - t0
+        est = t_rope + n_blocks * max(t_blk, 0.0) + (T / S) * t_ssm + (T / nr) * t_norm
+        per_role["global" if window <= 0 else "window"].append(est)
+        del q, k, v, part, ya, xc, ys
+    wall = time.perf_counter() - t_all0
+    n_g = sum(1 for w, _ in roles if w <= 0)
+    n_w = len(roles) - n_g
+    t_stack = (n_g * sum(per_role["global"]) / len(per_role["global"])
+               + n_w * sum(per_role["window"]) / len(per_role["window"]))
+    return {"value": shape.B * shape.T * len(roles) / t_stack, "unit": "tokens/s",
+            "cores": blas_threads() or 1, "host_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "seconds_per_stack_estimated": t_stack,
+            "sample": (f"stack32-b2-t16512 layers {list(CPU_STACK_LAYERS)}: per layer the "
+                       f"oracle attention over one {CPU_QUERY_BLOCK}-row query block plus its "
+                       f"K rotation, and conv + scan + norm over the first {CPU_SCAN_ROWS} "
+                       f"rows; extrapolated to {n_blocks} blocks and {T} rows per layer, then "
+                       f"to {n_g} global + {n_w} window layers; {wall:.1f} s of CPU work; "
+                       "tokens/s per layer as the GPU value")}
+
+
+def cpu_baseline_decode(shape, runs: int = 3):
+    """The oracle's decode step through the producer / consumer pair on the
+    decode workload (host inputs from the same generator), median of `runs`."""
+    import oracle
+    from workloads import decode_inputs
+    d = decode_inputs(shape, 0)
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        ra = oracle.mixer_step(d["a"], d["k_cache"], d["v_cache"], shape.n_prev, shape.M,
+                               shape.W, True, rope_base=shape.rope_base, eps=shape.eps)
+        oracle.mixer_step(d["b"], ra["k_cache"], ra["v_cache"], shape.n_prev, shape.M, shape.W,
+                          False, rope_base=shape.rope_base, eps=shape.eps)
+        ts.append(time.perf_counter() - t0)
+    med = sorted(ts)[len(ts) // 2]
+    return {"value": 1.0 / med, "unit": "steps/s", "cores": blas_threads() or 1,
+            "kind": "oracle",
+            "sample": f"{runs} whole decode steps (both layers of the pair, B={shape.B}) of "
+                      f"{shape.name}, median"}
+
+
+def alu_probe(hm_dir: str):
+    """Measured instruction rates of the vector ALU (libhm_probe.so): the
+    transcendental rate, the fused multiply-add rate and the selective scan's
+    single-pass mix (20 transcendental + 77 other VALU per token-channel), each
+    over 2048 workgroups of 256 lanes (8 waves per SIMD) timed with HIP events."""
+    import ctypes
+    import torch
+    path = os.path.join(hm_dir, "libhm_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.hm_probe_alu.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+    lib.hm_probe_alu_counts.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                        ctypes.POINTER(ctypes.c_int)]
+    blocks = 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    res = {}
+    for mode, name, iters in ((0, "exp", 4000), (1, "fma", 4000), (2, "scan_mix", 60)):
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        call = lambda: lib.hm_probe_alu(mode, ctypes.c_void_p(out.data_ptr()), blocks, iters, st)
+        assert call() == 0
+        ms = timed(call, 5, 2)
+        tr, va = ctypes.c_int(), ctypes.c_int()
+        lib.hm_probe_alu_counts(mode, ctypes.byref(tr), ctypes.byref(va))
+        lanes = blocks * 256 * iters
+        res[name] = {"trans_lane_ops_per_s": lanes * tr.value / (ms * 1e-3),
+                     "valu_lane_ops_per_s": lanes * va.value / (ms * 1e-3), "ms": ms}
+    # the scan mix: 8 token-channels per lane per iteration
+    res["scan_mix"]["token_channels_per_s"] = blocks * 256 * 60 * 8 / (res["scan_mix"]["ms"] * 1e-3)
+    res["note"] = ("lane-ops/s over the chip; 256 CUs x 64 lanes x 2.4 GHz = 3.93e13 is the "
+                   "nominal non-packed fp32 rate; the scan mix is run as written, so its "
+                   "token-channels/s is the ALU ceiling of a single-pass scan")
+    return res
 
 
 def run_prefill(shape, hm, t, steps, warmup, two_streams):
@@ -248,8 +363,19 @@ def run_prefill(shape, hm, t, steps, warmup, two_streams):
     return plan, ms
 
 
-def run_stack(shape, hm, steps, warmup):
-    """32 layers; sliding-window pairs share the producer's prepared K/V."""
+def make_events(n: int):
+    """n timing events, each created by one record() (the library records them
+    again on its own stream)."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    return evs
+
+
+def stack_layers(shape, hm):
+    """Device inputs of the 32 layers (consumers without k, v) and the plan."""
     import torch
     from workloads import prefill_inputs_torch, stack_layer_roles
     roles = stack_layer_roles(shape)
@@ -259,11 +385,53 @@ def run_stack(shape, hm, steps, warmup):
         if src != layer:
             del t["k"], t["v"]
         layers.append(t)
-    # one stream: every layer takes the fused three-launch sequence (measured
-    # 26.2 ms against 28.0 ms with the SSM branch on a second stream)
+    # one stream: every layer takes the fused three-launch sequence
     stack = hm.StackPlan(layers, roles, shape.M, shape.rope_base, shape.eps)
-    ms = timed(stack.run, steps, warmup)
-    return ms, len(roles)
+    return layers, roles, stack
+
+
+def time_stack(stack, roles, steps, warmup, launches=("attn_final",)):
+    """K passes of the stack with the library recording events around the
+    given launches of every layer (distinct events per pass, read after the
+    timed region).  Returns ms per pass (events around all passes), the mean
+    microseconds of each of those launches per layer role (global / window)
+    and the number of layers of each role."""
+    import torch
+    for _ in range(warmup):
+        stack.run()
+    n_l = len(roles)
+    names = ("prep_agg", "attn_final", "norm_mean")
+    want = [i for i in range(4) if any(names[j] in launches for j in (i - 1, i) if 0 <= j < 3)]
+    evs = make_events(steps * n_l * len(want))
+    per = []
+    it = iter(evs)
+    for k in range(steps):
+        row = []
+        for l in range(n_l):
+            row.append([next(it) if i in want else None for i in range(4)])
+        per.append(row)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for k in range(steps):
+        stack.run(events=per[k])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kinds = {}
+    for k in range(steps):
+        for l, (w, src) in enumerate(roles):
+            key = "global" if w <= 0 else "window"
+            ev = per[k][l]
+            d = kinds.setdefault(key, {n: [] for n in launches})
+            for j, n in enumerate(names):
+                if n in launches:
+                    d[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+    us = {key: {n: sum(v) / len(v) for n, v in d.items()} for key, d in kinds.items()}
+    counts = {"global": sum(1 for w, _ in roles if w <= 0),
+              "window": sum(1 for w, _ in roles if w > 0)}
+    return ms, us, counts
 
 
 def block_matmul_flops(shape, producer: bool = True) -> float:
@@ -309,15 +477,108 @@ def run_blocks(shape, hm, n_layers, steps, warmup):
     return ms, len(roles), fl_mm, fl_at
 
 
+def mfma_roofline(flop, us, kernel, launches, traffic=None, **extra):
+    achieved = flop / (us * 1e-6) / 1e12
+    d = {"bound": "mfma", "kernel": kernel, "launches": launches, "achieved": achieved,
+         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+         "traffic": traffic, "algorithmic_flop_per_launch": flop, "us_per_launch": us}
+    d.update(extra)
+    return d
+
+
+def layer_events(plan, steps, warmup):
+    """Mean microseconds of the three launches of one layer, from the events
+    the library records on its stream (distinct events per call)."""
+    import torch
+    for _ in range(warmup):
+        plan.run()
+    evs = make_events(4 * steps)
+    torch.cuda.synchronize()
+    for k in range(steps):
+        plan.run(events=evs[4 * k:4 * k + 4])
+    torch.cuda.synchronize()
+    out = {"prep_agg": 0.0, "attn_final": 0.0, "norm_mean": 0.0}
+    for k in range(steps):
+        e = evs[4 * k:4 * k + 4]
+        out["prep_agg"] += e[0].elapsed_time(e[1]) * 1e3 / steps
+        out["attn_final"] += e[1].elapsed_time(e[2]) * 1e3 / steps
+        out["norm_mean"] += e[2].elapsed_time(e[3]) * 1e3 / steps
+    return out
+
+
+def counters_run(hm, torch):
+    """Calibration copies, then 3 launches each of the kernels whose counters
+    profiles/ holds (for rocprofv3 --pmc runs; prints no JSON)."""
+    from workloads import (BLOCK_STACK, DECODE_PAIR, GLOBAL_PREFILL, STACK, SWA_PREFILL,
+                           decode_inputs, prefill_inputs, prefill_inputs_torch, to_device, with_)
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    del src, dst
+    # swa-prefill layer, its attention alone and its SSM branch alone
+    shape = SWA_PREFILL
+    t = to_device(prefill_inputs(shape, 0), shape.dtype)
+    plan = hm.PrefillPlan(t, shape.M, shape.W, rope_base=shape.rope_base, eps=shape.eps)
+    for _ in range(3):
+        plan.run()
+    for _ in range(3):
+        hm.attn_with_kv(t["q"], plan.kv, shape.Hkv, shape.M, shape.W, shape.rope_base,
+                        out=plan.ya)
+    for _ in range(3):
+        hm.conv_selective_scan(t["x"], t["conv_w"], t["conv_b"], t["delta"], t["A"], t["Bm"],
+                               t["Cm"], t["D"], t["z"], out=plan.ys)
+    del plan, t
+    # global-prefill layer and its attention alone
+    shape = GLOBAL_PREFILL
+    t = to_device(prefill_inputs(shape, 0), shape.dtype)
+    plan = hm.PrefillPlan(t, shape.M, shape.W, rope_base=shape.rope_base, eps=shape.eps)
+    for _ in range(3):
+        plan.run()
+    for _ in range(3):
+        hm.attn_with_kv(t["q"], plan.kv, shape.Hkv, shape.M, shape.W, shape.rope_base,
+                        out=plan.ya)
+    del plan, t
+    # one window layer and one global layer at the stack's size
+    for w in (STACK.W, 0):
+        shape = with_(STACK, W=w)
+        t = prefill_inputs_torch(shape, 0, 1 if w > 0 else 0, torch.device("cuda"))
+        plan = hm.PrefillPlan(t, shape.M, shape.W, rope_base=shape.rope_base, eps=shape.eps,
+                              want_states=False)
+        for _ in range(3):
+            plan.run()
+        del plan, t
+    torch.cuda.empty_cache()
+    # decode pair
+    dshape = DECODE_PAIR
+    d = to_device(decode_inputs(dshape, 0), dshape.dtype)
+    pa = hm.StepPlan(d["a"], d["k_cache"], d["v_cache"], dshape.n_prev, dshape.M, dshape.W)
+    pb = hm.StepPlan(d["b"], d["k_cache"], d["v_cache"], dshape.n_prev, dshape.M, dshape.W)
+    for _ in range(3):
+        pa.run()
+        pb.run()
+    del pa, pb, d
+    # the block stack's in-projection
+    x, w, segs = block_in_proj_operands(BLOCK_STACK)
+    outs = [torch.empty((x.shape[0], c), dtype=torch.bfloat16, device="cuda") for c in segs]
+    for _ in range(3):
+        hm.linear(x, w, seg_cols=segs, outs=outs)
+    torch.cuda.synchronize()
+    print("counters run done: 3 copies of", COPY_BYTES, "bytes, then 3 each of: swa-prefill "
+          "layer, its attention, its SSM branch; global-prefill layer, its attention; a window "
+          "and a global layer of the stack; the decode pair; the block-stack in-projection")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--quick", action="store_true", help="skip the global-prefill and stack lines")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--quick", action="store_true",
+                    help="skip the block and block-stack lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true",
-                    help="only a 256 MiB device copy (calibration) and the kernels whose HBM "
+                    help="only a 256 MiB device copy (calibration) and the kernels whose "
                          "counters profiles/ holds, for rocprofv3 --pmc runs; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -329,164 +590,38 @@ def main():
     import torch
     import hybrid_head_lm_amd as hm
     from workloads import (BLOCK_STACK, BLOCK_SWA, DECODE_PAIR, GLOBAL_PREFILL, STACK,
-                           SWA_PREFILL, decode_inputs, prefill_inputs, to_device)
+                           SWA_PREFILL, decode_inputs, prefill_inputs, to_device, with_)
 
     torch.cuda.set_device(0)
-    shape = SWA_PREFILL
-    inp = prefill_inputs(shape, 0)
-    t = to_device(inp, shape.dtype)
-
     if args.counters:
-        plan = hm.PrefillPlan(t, shape.M, shape.W, rope_base=shape.rope_base, eps=shape.eps)
-        plan.run()
-        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        for _ in range(3):
-            hm.attn_with_kv(t["q"], plan.kv, shape.Hkv, shape.M, shape.W, shape.rope_base,
-                            out=plan.ya)
-        for _ in range(3):
-            hm.conv_selective_scan(t["x"], t["conv_w"], t["conv_b"], t["delta"], t["A"],
-                                   t["Bm"], t["Cm"], t["D"], t["z"], out=plan.ys)
-        for _ in range(3):
-            plan.run()
-        dshape = DECODE_PAIR
-        d = to_device(decode_inputs(dshape, 0), dshape.dtype)
-        pa = hm.StepPlan(d["a"], d["k_cache"], d["v_cache"], dshape.n_prev, dshape.M, dshape.W)
-        pb = hm.StepPlan(d["b"], d["k_cache"], d["v_cache"], dshape.n_prev, dshape.M, dshape.W)
-        for _ in range(3):
-            pa.run()
-            pb.run()
-        del pa, pb, d
-        x, w, segs = block_in_proj_operands(BLOCK_STACK)
-        outs = [torch.empty((x.shape[0], c), dtype=torch.bfloat16, device="cuda") for c in segs]
-        for _ in range(3):
-            hm.linear(x, w, seg_cols=segs, outs=outs)
-        torch.cuda.synchronize()
-        print("counters run done: 3 copies of", COPY_BYTES, "bytes, then 3 each of the "
-              "attention launch, the SSM branch, the fused layer, the decode pair and the "
-              "block-stack in-projection")
+        counters_run(hm, torch)
         return
 
-    # the step: one mixer layer (both branches on one stream, kernels in order)
-    plan, ms = run_prefill(shape, hm, t, args.steps, args.warmup, two_streams=False)
-    sclk = []
-    layer_dist = step_percentiles(plan.run, max(200, args.steps),
-                                  while_busy=lambda: sample_sclk(sclk))
-    cur = [c for c, _ in sclk if c is not None]
-    sclk = {"max_sampled": max(cur) if cur else None,
-            "highest_level": sclk[0][1] if sclk else None,
-            "note": "the driver's current-clock line (S:), read 12 times 1 ms apart while "
-                    "the layer calls run; it reads far below the highest level and below what "
-                    "the measured MFMA rates need, so it is an average that includes idle "
-                    "time, not the clock during the kernels"}
-    _, ms_two = run_prefill(shape, hm, t, args.steps, args.warmup, two_streams=True)
-    tokens = shape.B * shape.T
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    # the same layer with the meta tokens cached: only the N real-token rows are
-    # computed, from the meta rows' K/V and the SSM-branch states after them
-    from workloads import cached_meta_inputs
-    _, ctok, cmeta = cached_meta_inputs(shape, 0)
-    ct = to_device(ctok, shape.dtype)
-    cmk = to_device({"k": cmeta["k"], "v": cmeta["v"]}, shape.dtype)
-    cst = torch.zeros((shape.B, shape.Di, shape.K - 1), dtype=torch.float32, device="cuda")
-    ch0 = torch.zeros((shape.B, shape.Di, shape.Ns), dtype=torch.float32, device="cuda")
-    cplan = hm.PrefillPlan(ct, shape.M, shape.W, rope_base=shape.rope_base, eps=shape.eps,
-                           want_states=False, meta={"k": cmk["k"], "v": cmk["v"]},
-                           conv_state_in=cst, h0=ch0)
-    ms_cached = timed(cplan.run, args.steps, args.warmup)
-    del cplan, ct, cmk
-
-    # the projections around the layer: in-projection of the 2176 rows from width
-    # 1600 into Q, K, V, x, z (5440 columns) and the out-projection (1600 -> 1600)
-    gen = torch.Generator(device="cuda").manual_seed(3)
-    d_model = shape.Hq * shape.Dh
-    segs = [shape.Hq * shape.Dh, shape.Hkv * shape.Dh, shape.Hkv * shape.Dh, shape.Di, shape.Di]
-    px = torch.randn(shape.B * shape.T, d_model, device="cuda", generator=gen).bfloat16()
-    pw_in = (torch.randn(sum(segs), d_model, device="cuda", generator=gen)
-             / d_model ** 0.5).bfloat16()
-    pw_out = (torch.randn(d_model, shape.Di, device="cuda", generator=gen)
-              / shape.Di ** 0.5).bfloat16()
-    pouts = [torch.empty(shape.B * shape.T, c, dtype=torch.bfloat16, device="cuda") for c in segs]
-    py = torch.empty(shape.B * shape.T, d_model, dtype=torch.bfloat16, device="cuda")
-    ms_in = timed(lambda: hm.linear(px, pw_in, seg_cols=segs, outs=pouts), args.steps, args.warmup)
-    ms_out = timed(lambda: hm.linear(pouts[3], pw_out, outs=[py]), args.steps, args.warmup)
-    fl_in = 2.0 * shape.B * shape.T * sum(segs) * d_model
-    fl_out = 2.0 * shape.B * shape.T * d_model * shape.Di
-    del px, pw_in, pw_out, pouts, py
-
-    # dominant kernel on its own: attention over the prepared K/V
-    ms_attn = timed(lambda: hm.attn_with_kv(t["q"], plan.kv, shape.Hkv, shape.M, shape.W,
-                                            shape.rope_base, out=plan.ya),
-                    args.steps, args.warmup)
-    fl = attn_flops(shape)
-    achieved = fl / (ms_attn * 1e-3) / 1e12
-    traffic = traffic_from_profile(ATTN_SOURCES, "attn_fwd_bf16.swa-prefill-b1-t2176.pmc.txt")
-
-    # SSM branch and fusion on their own (context for the breakdown)
-    tc_ssm = shape.B * shape.T * shape.Di
-    ms_ssm = timed(lambda: hm.conv_selective_scan(t["x"], t["conv_w"], t["conv_b"], t["delta"],
-                                                  t["A"], t["Bm"], t["Cm"], t["D"], t["z"],
-                                                  out=plan.ys), args.steps, args.warmup)
-    ms_norm = timed(lambda: hm.branch_norm_mean(plan.ya, plan.ys, t["beta_a"], t["beta_s"],
-                                                shape.eps, out=plan.out), args.steps, args.warmup)
-
-    # decode: one token through the producer / consumer pair
-    dshape = DECODE_PAIR
-    d = to_device(decode_inputs(dshape, 0), dshape.dtype)
-    pa = hm.StepPlan(d["a"], d["k_cache"], d["v_cache"], dshape.n_prev, dshape.M, dshape.W,
-                     rope_base=dshape.rope_base, eps=dshape.eps)
-    pb = hm.StepPlan(d["b"], d["k_cache"], d["v_cache"], dshape.n_prev, dshape.M, dshape.W,
-                     rope_base=dshape.rope_base, eps=dshape.eps)
-
-    def decode_step():
-        pa.run()
-        pb.run()
-    ms_dec = timed(decode_step, args.steps, args.warmup)
-    dbytes = decode_bytes(dshape)
-    # cold: before every step a 512 MB write evicts the pair's cache and states
-    # from the 256 MB Infinity Cache, as the other layers of a model would, and a
-    # 1 GB read then leaves the cache holding clean lines (the other layers
-    # mostly read weights and caches), so the step does not pay for writing back
-    # the flush's dirty lines
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-    flush_rd = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    cold = []
-    for i in range(args.warmup + args.steps):
-        flush.fill_(i & 0xFF)
-        flush_rd.max()
-        e0.record()
-        decode_step()
-        e1.record()
-        torch.cuda.synchronize()
-        if i >= args.warmup:
-            cold.append(e0.elapsed_time(e1))
-    ms_dec_cold = sum(cold) / len(cold)
-    del flush, flush_rd
-
-    # ragged decode: the same pair with one n_prev per sequence, uniform over
-    # 0 .. 2047 (seeded), back to back
-    import numpy as np
-    nps = np.random.default_rng(5).integers(0, 2048, size=dshape.B).astype(np.int32)
-    npt = torch.from_numpy(nps).cuda()
-    ra_plan = hm.StepPlan(d["a"], d["k_cache"], d["v_cache"], int(nps.max()), dshape.M, dshape.W,
-                          rope_base=dshape.rope_base, eps=dshape.eps, n_prev_seq=npt)
-    rb_plan = hm.StepPlan(d["b"], d["k_cache"], d["v_cache"], int(nps.max()), dshape.M, dshape.W,
-                          rope_base=dshape.rope_base, eps=dshape.eps, n_prev_seq=npt)
-
-    def ragged_step():
-        ra_plan.run()
-        rb_plan.run()
-    ms_rag = timed(ragged_step, args.steps, args.warmup)
-    rag_bytes = decode_bytes(dshape, nps)
-    del ra_plan, rb_plan
-
+    # ------------------------------------------------------------ the step:
+    # one pass of the 32-layer stack, the library recording its launch
+    # boundaries; a second, uninstrumented timing beside it
+    shape = STACK
+    layers, roles, stack = stack_layers(shape, hm)
+    log("stack inputs ready")
+    ms, us, counts = time_stack(stack, roles, args.steps, args.warmup)
+    ms_plain = timed(stack.run, args.steps, 1)
+    _, us_all, _ = time_stack(stack, roles, max(3, args.steps // 4), 1,
+                              launches=("prep_agg", "attn_final", "norm_mean"))
+    log(f"stack {ms:.3f} ms per pass (uninstrumented {ms_plain:.3f})")
+    n_layers = len(roles)
+    rows = shape.B * shape.T
+    fl_w = attn_flops(with_(shape, W=shape.W))
+    fl_g = attn_flops(with_(shape, W=0))
+    fused_traffic = traffic_from_profile(FUSED_SOURCES, "prefill_attn_final.stack32-window.pmc.txt")
+    fused_traffic_g = traffic_from_profile(FUSED_SOURCES,
+                                           "prefill_attn_final.stack32-global.pmc.txt")
+    kern_ms = {k: sum(counts[r] * us[r][k] for r in us) / 1e3 for k in ("attn_final",)}
     result = {
         "metric": "hybrid-mixer prefill tokens/s per layer + decode steps/s; % MFMA/HBM roofline",
-        "value": tokens / (ms * 1e-3),
+        "value": rows * n_layers / (ms * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -497,110 +632,258 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": shape.name, "batch": shape.B, "meta_tokens": shape.M,
-                   "tokens": shape.N, "rows": shape.T, "q_heads": shape.Hq,
-                   "kv_heads": shape.Hkv, "head_dim": shape.Dh, "window": shape.W,
-                   "ssm_width": shape.Di, "ssm_states": shape.Ns, "conv": shape.K,
-                   "branches": "attention then SSM on one stream"},
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd_bf16", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "algorithmic_flop_per_launch": fl, "ms_per_launch": ms_attn},
-        "cached_meta": {"workload": shape.name + " with the 128 meta rows cached",
-                        "real_tokens_per_s": shape.B * shape.N / (ms_cached * 1e-3),
-                        "ms_per_layer": ms_cached,
-                        "full_layer_real_tokens_per_s": shape.B * shape.N / (ms * 1e-3)},
-        "projections": {
-            "workload": shape.name + " in-projection 1600 -> Q, K, V, x, z (5440) and "
-                                     "out-projection 1600 -> 1600, bf16",
-            "in_proj": {"ms": ms_in, "achieved": fl_in / (ms_in * 1e-3) / 1e12,
-                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                        "frac": fl_in / (ms_in * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
-            "out_proj": {"ms": ms_out, "achieved": fl_out / (ms_out * 1e-3) / 1e12,
-                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": fl_out / (ms_out * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}},
-        "layer_step_us": layer_dist,
-        "sclk_mhz": sclk,
-        "breakdown_ms": {"layer_one_stream": ms, "layer_two_streams": ms_two,
-                         "attention_kernel": ms_attn, "ssm_branch": ms_ssm,
-                         "norm_mean": ms_norm},
-        "ssm_branch": {"bound": "hbm", "achieved": scan_bytes(shape) / (ms_ssm * 1e-3) / 1e9,
-                       "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                       "frac": scan_bytes(shape) / (ms_ssm * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                       "traffic": traffic_from_profile(
-                           SSM_SOURCES, "ssm-branch.swa-prefill-b1-t2176.pmc.txt",
-                           "hbm_bytes_per_call"),
-                       "alu": {"bound": "alu", "unit": "lane-op/s",
-                               "valu_per_token_channel": SCAN_VALU_PER_TC,
-                               "transcendental_per_token_channel": SCAN_TRANS_PER_TC,
-                               "achieved": tc_ssm * (SCAN_VALU_PER_TC + SCAN_TRANS_PER_TC)
-                                           / (ms_ssm * 1e-3),
-                               "peak": PEAK_VALU_LANE_OPS,
-                               "frac": tc_ssm * (SCAN_VALU_PER_TC + SCAN_TRANS_PER_TC)
-                                       / (ms_ssm * 1e-3) / PEAK_VALU_LANE_OPS}},
-        "decode": {"workload": dshape.name, "steps_per_s": 1e3 / ms_dec_cold,
-                   "tokens_per_s": dshape.B * 1e3 / ms_dec_cold, "ms_per_step": ms_dec_cold,
-                   "cache": "cold (Infinity Cache flushed before every step: 512 MB "
-                            "written, then 1 GB read)",
-                   "roofline": {"bound": "hbm",
-                                "achieved": dbytes / (ms_dec_cold * 1e-3) / 1e9,
-                                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                "frac": dbytes / (ms_dec_cold * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                                "algorithmic_bytes_per_step": dbytes,
-                                "traffic": traffic_from_profile(
-                                    STEP_SOURCES, "step-pair.decode-pair-b64-cache1152.pmc.txt",
-                                    "hbm_bytes_per_step")},
-                   "warm": {"steps_per_s": 1e3 / ms_dec, "ms_per_step": ms_dec,
-                            "hbm_frac": dbytes / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                            "note": "back-to-back steps; the 222 MB of the pair stay in the "
-                                    "256 MB Infinity Cache"}},
-        "ragged_decode": {"workload": dshape.name + " with n_prev per sequence uniform "
-                                                    "over 0..2047 (seeded)",
-                          "steps_per_s": 1e3 / ms_rag, "ms_per_step": ms_rag,
-                          "hbm_frac": rag_bytes / (ms_rag * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                          "algorithmic_bytes_per_step": rag_bytes,
-                          "cache": "warm (back-to-back steps)"},
+        "config": {"workload": shape.name, "layers": n_layers,
+                   "global_layers": list(shape.global_layers), "batch": shape.B,
+                   "meta_tokens": shape.M, "tokens": shape.N, "rows": shape.T,
+                   "q_heads": shape.Hq, "kv_heads": shape.Hkv, "head_dim": shape.Dh,
+                   "window": shape.W, "ssm_width": shape.Di, "ssm_states": shape.Ns,
+                   "conv": shape.K,
+                   "kv_sharing": "window layers paired (1,2)..(13,14), (16,17)..(28,29); "
+                                 "layer 30 alone",
+                   "step": "one pass of the 32 mixer layers, three launches per layer on one "
+                           "stream; value = rows x layers / pass time (tokens/s per layer)"},
+        "ms_per_step_uninstrumented": ms_plain,
+        "timing": "HIP events around the K timed passes; inside them the library records "
+                  "two more events per layer around its middle launch (the roofline); "
+                  "ms_per_step_uninstrumented is the same stack timed without them",
+        "roofline": mfma_roofline(
+            fl_w, us["window"]["attn_final"], "prefill_attn_final",
+            f"the {counts['window']} window layers of each pass (attention | final scan "
+            "pass of the SSM branch in one launch; FLOPs count the attention only)",
+            traffic=fused_traffic,
+            final_scan_bytes_per_launch=scan_bytes(shape),
+            share_of_step_all_layers=kern_ms["attn_final"] / ms,
+            timing="HIP events the library records on its stream around this launch in every "
+                   "layer of every timed pass",
+            **{"global": mfma_roofline(fl_g, us["global"]["attn_final"], "prefill_attn_final",
+                                       f"the {counts['global']} global layers of each pass",
+                                       traffic=fused_traffic_g)}),
+        "stack_kernels_us": us_all,
+        "stack_kernels_ms_per_pass": {
+            f"{k}_{r}": counts[r] * us_all[r][k] / 1e3 for r in us_all for k in us_all[r]},
+        "stack_kernels_note": "from separate passes with events around all three launches "
+                              "of every layer, after the timed region",
     }
-    del pa, pb, d
+    if not args.no_cpu_baseline:
+        log("cpu baseline (stack sample)")
+        result["cpu_baseline"] = cpu_baseline_stack(shape, layers, roles)
+    del stack, layers
+    torch.cuda.empty_cache()
 
-    # one whole block at the model card's widths over the same rows
-    bshape = BLOCK_SWA
-    bms, _, bfl_mm, bfl_at = run_blocks(bshape, hm, 1, args.steps, args.warmup)
-    result["block"] = {
-        "workload": bshape.name + " (width 1600, FFN 5504; norm, projections, mixer, norm, FFN)",
-        "tokens_per_s": bshape.B * bshape.T / (bms * 1e-3), "ms_per_block": bms,
-        "mixer_ms": ms, "matmul_tflop": bfl_mm / 1e12,
-        "tflops": (bfl_mm + bfl_at) / (bms * 1e-3) / 1e12,
-        "frac_mfma": (bfl_mm + bfl_at) / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    # ------------------------------------------------------------ swa-prefill layer
+    log("swa-prefill layer")
+    sshape = SWA_PREFILL
+    inp = prefill_inputs(sshape, 0)
+    t = to_device(inp, sshape.dtype)
+    lsteps = max(50, args.steps)
+    plan, ms_l = run_prefill(sshape, hm, t, lsteps, 10, two_streams=False)
+    sclk = []
+    layer_dist = step_percentiles(plan.run, 200, while_busy=lambda: sample_sclk(sclk))
+    cur = [c for c, _ in sclk if c is not None]
+    _, ms_two = run_prefill(sshape, hm, t, lsteps, 10, two_streams=True)
+    lev = layer_events(plan, lsteps, 5)
+    fl = attn_flops(sshape)
+    ms_attn = timed(lambda: hm.attn_with_kv(t["q"], plan.kv, sshape.Hkv, sshape.M, sshape.W,
+                                            sshape.rope_base, out=plan.ya), lsteps, 10)
+    ms_ssm = timed(lambda: hm.conv_selective_scan(t["x"], t["conv_w"], t["conv_b"], t["delta"],
+                                                  t["A"], t["Bm"], t["Cm"], t["D"], t["z"],
+                                                  out=plan.ys), lsteps, 10)
+    ms_norm = timed(lambda: hm.branch_norm_mean(plan.ya, plan.ys, t["beta_a"], t["beta_s"],
+                                                sshape.eps, out=plan.out), lsteps, 10)
+    result["swa_prefill"] = {
+        "workload": sshape.name, "tokens_per_s": sshape.B * sshape.T / (ms_l * 1e-3),
+        "ms_per_layer": ms_l, "layer_step_us": layer_dist,
+        "kernels_us": lev,
+        "roofline": mfma_roofline(fl, lev["attn_final"], "prefill_attn_final",
+                                  "the layer's middle launch (attention | final scan)"),
+        "attention_alone": mfma_roofline(
+            fl, ms_attn * 1e3, "attn_fwd_bf16", "attention alone over the prepared K/V",
+            traffic=traffic_from_profile(ATTN_SOURCES,
+                                         "attn_fwd_bf16.swa-prefill-b1-t2176.pmc.txt")),
+        "breakdown_ms": {"layer_one_stream": ms_l, "layer_two_streams": ms_two,
+                         "attention_kernel": ms_attn, "ssm_branch": ms_ssm, "norm_mean": ms_norm},
+        "sclk_mhz": {"max_sampled": max(cur) if cur else None,
+                     "highest_level": sclk[0][1] if sclk else None,
+                     "note": "the driver's current-clock line, read 12 times 1 ms apart while "
+                             "layer calls run: an average including idle time"}}
+
+    # the same layer with the meta tokens cached (real-token rows only)
+    from workloads import cached_meta_inputs
+    _, ctok, cmeta = cached_meta_inputs(sshape, 0)
+    ct = to_device(ctok, sshape.dtype)
+    cmk = to_device({"k": cmeta["k"], "v": cmeta["v"]}, sshape.dtype)
+    cst = torch.zeros((sshape.B, sshape.Di, sshape.K - 1), dtype=torch.float32, device="cuda")
+    ch0 = torch.zeros((sshape.B, sshape.Di, sshape.Ns), dtype=torch.float32, device="cuda")
+    cplan = hm.PrefillPlan(ct, sshape.M, sshape.W, rope_base=sshape.rope_base, eps=sshape.eps,
+                           want_states=False, meta={"k": cmk["k"], "v": cmk["v"]},
+                           conv_state_in=cst, h0=ch0)
+    ms_cached = timed(cplan.run, lsteps, 10)
+    result["cached_meta"] = {"workload": sshape.name + " with the 128 meta rows cached",
+                             "real_tokens_per_s": sshape.B * sshape.N / (ms_cached * 1e-3),
+                             "ms_per_layer": ms_cached,
+                             "full_layer_real_tokens_per_s": sshape.B * sshape.N / (ms_l * 1e-3)}
+    del cplan, ct, cmk
+
+    # the projections around the layer
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    d_model = sshape.Hq * sshape.Dh
+    segs = [sshape.Hq * sshape.Dh, sshape.Hkv * sshape.Dh, sshape.Hkv * sshape.Dh, sshape.Di,
+            sshape.Di]
+    px = torch.randn(sshape.B * sshape.T, d_model, device="cuda", generator=gen).bfloat16()
+    pw_in = (torch.randn(sum(segs), d_model, device="cuda", generator=gen)
+             / d_model ** 0.5).bfloat16()
+    pw_out = (torch.randn(d_model, sshape.Di, device="cuda", generator=gen)
+              / sshape.Di ** 0.5).bfloat16()
+    pouts = [torch.empty(sshape.B * sshape.T, c, dtype=torch.bfloat16, device="cuda")
+             for c in segs]
+    py = torch.empty(sshape.B * sshape.T, d_model, dtype=torch.bfloat16, device="cuda")
+    ms_in = timed(lambda: hm.linear(px, pw_in, seg_cols=segs, outs=pouts), lsteps, 10)
+    ms_out = timed(lambda: hm.linear(pouts[3], pw_out, outs=[py]), lsteps, 10)
+    fl_in = 2.0 * sshape.B * sshape.T * sum(segs) * d_model
+    fl_out = 2.0 * sshape.B * sshape.T * d_model * sshape.Di
+    result["projections"] = {
+        "workload": sshape.name + " in-projection 1600 -> Q, K, V, x, z (5440) and "
+                                  "out-projection 1600 -> 1600, bf16",
+        "in_proj": mfma_roofline(fl_in, ms_in * 1e3, "linear_bf16_w4", "one call"),
+        "out_proj": mfma_roofline(fl_out, ms_out * 1e3, "linear_bf16", "one call")}
+    del px, pw_in, pw_out, pouts, py
+
+    # ------------------------------------------------------------ SSM branch and ALU ceiling
+    log("ssm branch and ALU probe")
+    probe = alu_probe(os.path.dirname(hm.LIB_PATH))
+    tc_ssm = sshape.B * sshape.T * sshape.Di
+    bound_tc = probe["scan_mix"]["token_channels_per_s"] if probe else None
+    result["ssm_branch"] = {
+        "workload": sshape.name + ": conv + selective scan alone (hm_conv_selective_scan)",
+        "bound": "hbm", "achieved": scan_bytes(sshape) / (ms_ssm * 1e-3) / 1e9,
+        "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+        "frac": scan_bytes(sshape) / (ms_ssm * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "ms": ms_ssm,
+        "traffic": traffic_from_profile(SSM_SOURCES, "ssm-branch.swa-prefill-b1-t2176.pmc.txt",
+                                        "hbm_bytes_per_call"),
+        "alu": {"bound": "alu", "unit": "token-channels/s",
+                "achieved": tc_ssm / (ms_ssm * 1e-3), "peak": bound_tc,
+                "frac": (tc_ssm / (ms_ssm * 1e-3) / bound_tc) if bound_tc else None,
+                "peak_source": "measured: the scan's single-pass instruction mix per "
+                               "token-channel (20 transcendental + 77 other VALU) run on every "
+                               "SIMD (alu_probe.scan_mix)",
+                "valu_per_token_channel": SCAN_VALU_PER_TC,
+                "transcendental_per_token_channel": SCAN_TRANS_PER_TC}}
+    result["alu_probe"] = probe
+    del plan, t
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ global-prefill layer
+    log("global-prefill layer")
+    gshape = GLOBAL_PREFILL
+    gt = to_device(prefill_inputs(gshape, 0), gshape.dtype)
+    gsteps = max(5, args.steps // 2)
+    gplan, gms = run_prefill(gshape, hm, gt, gsteps, 2, two_streams=False)
+    gev = layer_events(gplan, gsteps, 1)
+    gms_attn = timed(lambda: hm.attn_with_kv(gt["q"], gplan.kv, gshape.Hkv, gshape.M, gshape.W,
+                                             gshape.rope_base, out=gplan.ya), gsteps, 2)
+    gfl = attn_flops(gshape)
+    result["global_prefill"] = {
+        "workload": gshape.name, "tokens_per_s": gshape.B * gshape.T / (gms * 1e-3),
+        "ms_per_layer": gms, "kernels_us": gev,
+        "roofline": mfma_roofline(gfl, gev["attn_final"], "prefill_attn_final",
+                                  "the layer's middle launch (attention | final scan)"),
+        "attention_alone": mfma_roofline(gfl, gms_attn * 1e3, "attn_fwd_bf16",
+                                         "attention alone over the prepared K/V")}
+    del gt, gplan
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ decode
+    log("decode")
+    dshape = DECODE_PAIR
+    d = to_device(decode_inputs(dshape, 0), dshape.dtype)
+    pa = hm.StepPlan(d["a"], d["k_cache"], d["v_cache"], dshape.n_prev, dshape.M, dshape.W,
+                     rope_base=dshape.rope_base, eps=dshape.eps)
+    pb = hm.StepPlan(d["b"], d["k_cache"], d["v_cache"], dshape.n_prev, dshape.M, dshape.W,
+                     rope_base=dshape.rope_base, eps=dshape.eps)
+
+    def decode_step():
+        pa.run()
+        pb.run()
+    dsteps = max(50, args.steps)
+    ms_dec = timed(decode_step, dsteps, 10)
+    dbytes = decode_bytes(dshape)
+    # cold: before every step a 512 MB write evicts the pair's cache and states
+    # from the 256 MB Infinity Cache, as the other layers of a model would, and a
+    # 1 GB read then leaves the cache holding clean lines
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush_rd = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    cold = []
+    for i in range(10 + dsteps):
+        flush.fill_(i & 0xFF)
+        flush_rd.max()
+        e0.record()
+        decode_step()
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 10:
+            cold.append(e0.elapsed_time(e1))
+    ms_dec_cold = sum(cold) / len(cold)
+    del flush, flush_rd
+    result["decode"] = {
+        "workload": dshape.name, "steps_per_s": 1e3 / ms_dec_cold,
+        "tokens_per_s": dshape.B * 1e3 / ms_dec_cold, "ms_per_step": ms_dec_cold,
+        "cache": "cold (Infinity Cache flushed before every step: 512 MB written, then 1 GB "
+                 "read)",
+        "roofline": {"bound": "hbm", "achieved": dbytes / (ms_dec_cold * 1e-3) / 1e9,
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": dbytes / (ms_dec_cold * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                     "algorithmic_bytes_per_step": dbytes,
+                     "traffic": traffic_from_profile(
+                         STEP_SOURCES, "step-pair.decode-pair-b64-cache1152.pmc.txt",
+                         "hbm_bytes_per_step")},
+        "warm": {"steps_per_s": 1e3 / ms_dec, "ms_per_step": ms_dec,
+                 "hbm_frac": dbytes / (ms_dec * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                 "note": "back-to-back steps; the 222 MB of the pair stay in the 256 MB "
+                         "Infinity Cache"}}
+    nps = np.random.default_rng(5).integers(0, 2048, size=dshape.B).astype(np.int32)
+    npt = torch.from_numpy(nps).cuda()
+    ra_plan = hm.StepPlan(d["a"], d["k_cache"], d["v_cache"], int(nps.max()), dshape.M, dshape.W,
+                          rope_base=dshape.rope_base, eps=dshape.eps, n_prev_seq=npt)
+    rb_plan = hm.StepPlan(d["b"], d["k_cache"], d["v_cache"], int(nps.max()), dshape.M, dshape.W,
+                          rope_base=dshape.rope_base, eps=dshape.eps, n_prev_seq=npt)
+
+    def ragged_step():
+        ra_plan.run()
+        rb_plan.run()
+    ms_rag = timed(ragged_step, dsteps, 10)
+    rag_bytes = decode_bytes(dshape, nps)
+    result["ragged_decode"] = {
+        "workload": dshape.name + " with n_prev per sequence uniform over 0..2047 (seeded)",
+        "steps_per_s": 1e3 / ms_rag, "ms_per_step": ms_rag,
+        "hbm_frac": rag_bytes / (ms_rag * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "algorithmic_bytes_per_step": rag_bytes, "cache": "warm (back-to-back steps)"}
+    del ra_plan, rb_plan, pa, pb, d
+    if not args.no_cpu_baseline:
+        log("cpu baseline (decode)")
+        result["cpu_baseline_decode"] = cpu_baseline_decode(dshape)
     torch.cuda.empty_cache()
 
     if not args.quick:
-        gshape = GLOBAL_PREFILL
-        gt = to_device(prefill_inputs(gshape, 0), gshape.dtype)
-        gsteps = max(3, args.steps // 5)
-        gplan, gms = run_prefill(gshape, hm, gt, gsteps, 2, two_streams=False)
-        gms_attn = timed(lambda: hm.attn_with_kv(gt["q"], gplan.kv, gshape.Hkv, gshape.M,
-                                                 gshape.W, gshape.rope_base, out=gplan.ya),
-                         gsteps, 2)
-        gfl = attn_flops(gshape)
-        result["global_prefill"] = {
-            "workload": gshape.name, "tokens_per_s": gshape.B * gshape.T / (gms * 1e-3),
-            "ms_per_layer": gms, "attention_tflops": gfl / (gms_attn * 1e-3) / 1e12,
-            "attention_frac_mfma": gfl / (gms_attn * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
-        del gt, gplan
+        log("blocks")
+        bshape = BLOCK_SWA
+        bms, _, bfl_mm, bfl_at = run_blocks(bshape, hm, 1, lsteps, 10)
+        result["block"] = {
+            "workload": bshape.name + " (width 1600, FFN 5504; norm, projections, mixer, "
+                                      "norm, FFN)",
+            "tokens_per_s": bshape.B * bshape.T / (bms * 1e-3), "ms_per_block": bms,
+            "mixer_ms": ms_l, "matmul_tflop": bfl_mm / 1e12,
+            "tflops": (bfl_mm + bfl_at) / (bms * 1e-3) / 1e12,
+            "frac_mfma": (bfl_mm + bfl_at) / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         torch.cuda.empty_cache()
-        sms, nl = run_stack(STACK, hm, 3, 1)
-        result["stack"] = {"workload": STACK.name, "layers": nl,
-                           "tokens_per_s_per_layer": STACK.B * STACK.T * nl / (sms * 1e-3),
-                           "ms_per_stack": sms,
-                           "inputs": "torch Philox generator on the device (same distributions)"}
-        torch.cuda.empty_cache()
-        kms, kl, kfl_mm, kfl_at = run_blocks(BLOCK_STACK, hm, BLOCK_STACK.layers, 3, 1)
-        # the block stack's dominant kernel: a producer block's in-projection on its own
+        kms, kl, kfl_mm, kfl_at = run_blocks(BLOCK_STACK, hm, BLOCK_STACK.layers, 5, 1)
         gx, gw, gsegs = block_in_proj_operands(BLOCK_STACK)
-        gouts = [torch.empty((gx.shape[0], c), dtype=torch.bfloat16, device="cuda") for c in gsegs]
-        gms = timed(lambda: hm.linear(gx, gw, seg_cols=gsegs, outs=gouts), 10, 2)
-        gfl = 2.0 * gx.shape[0] * gw.shape[0] * gx.shape[1]
+        gouts = [torch.empty((gx.shape[0], c), dtype=torch.bfloat16, device="cuda")
+                 for c in gsegs]
+        kgms = timed(lambda: hm.linear(gx, gw, seg_cols=gsegs, outs=gouts), 10, 2)
+        kgfl = 2.0 * gx.shape[0] * gw.shape[0] * gx.shape[1]
         del gx, gw, gouts
         result["block_stack"] = {
             "workload": BLOCK_STACK.name + " (32 whole blocks, width 1600, FFN 5504)",
@@ -609,19 +892,14 @@ def main():
             "tokens_per_s": BLOCK_STACK.B * BLOCK_STACK.T / (kms * 1e-3),
             "tflops": (kfl_mm + kfl_at) / (kms * 1e-3) / 1e12,
             "frac_mfma": (kfl_mm + kfl_at) / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-            "roofline": {"bound": "mfma", "kernel": "linear_bf16_w4",
-                         "launch": "a producer block's in-projection, 33024 x 1600 -> 5440",
-                         "achieved": gfl / (gms * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": gfl / (gms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                         "algorithmic_flop_per_launch": gfl, "ms_per_launch": gms,
-                         "traffic": traffic_from_profile(
-                             LINEAR_SOURCES, "linear_bf16_w4.block-stack32-in-proj.pmc.txt")},
+            "roofline": mfma_roofline(
+                kgfl, kgms * 1e3, "linear_bf16_w4",
+                "a producer block's in-projection, 33024 x 1600 -> 5440",
+                traffic=traffic_from_profile(LINEAR_SOURCES,
+                                             "linear_bf16_w4.block-stack32-in-proj.pmc.txt")),
             "inputs": "torch Philox generator on the device (same distributions)"}
         torch.cuda.empty_cache()
-
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(shape, inp)
-    print(json.dumps(result))
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

@@ -59,7 +59,7 @@ class PrefillArgs(ctypes.Structure):
                             "h_out", "kv")] + [("kv_bytes", _sz), ("kv_reuse", _i),
                                                ("stream2", _vp), ("workspace", _vp),
                                                ("workspace_bytes", _sz)] + [
-        (n, _vp) for n in ("meta_k", "meta_v", "conv_state_in", "h0")]
+        (n, _vp) for n in ("meta_k", "meta_v", "conv_state_in", "h0", "events")]
 
 
 class StepArgs(ctypes.Structure):

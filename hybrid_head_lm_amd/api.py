@@ -350,9 +350,22 @@ class PrefillPlan:
         a.workspace, a.workspace_bytes = self.ws.data_ptr(), self.ws.numel()
         self.args = a
 
-    def run(self, stream=None):
+    def run(self, stream=None, events=None):
+        """events: optional 4 torch.cuda.Event or None (timing enabled, already
+        created by one record()) that the library records around its three
+        launches (None entries are skipped)."""
         s = _stream() if stream is None else ctypes.c_void_p(stream.cuda_stream)
-        _check(lib.hm_mixer_prefill(ctypes.byref(self.args), s))
+        if events is None:
+            _check(lib.hm_mixer_prefill(ctypes.byref(self.args), s))
+            return self.out
+        if len(events) != 4:
+            raise ValueError("events: four torch.cuda.Event")
+        arr = (ctypes.c_void_p * 4)(*[None if e is None else e.cuda_event for e in events])
+        self.args.events = ctypes.cast(arr, ctypes.c_void_p)
+        try:
+            _check(lib.hm_mixer_prefill(ctypes.byref(self.args), s))
+        finally:
+            self.args.events = None
         return self.out
 
 

@@ -13,6 +13,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhm.so")
+# the benchmark's instruction-rate probe: its own library, not part of libhm
+PROBE_SRC = os.path.join(HERE, "probe", "alu_rate.hip")
+PROBE_LIB = os.path.join(HERE, "libhm_probe.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 ARCH = os.environ.get("HM_OFFLOAD_ARCH", "gfx950")
@@ -71,7 +74,21 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    """Compile the ALU instruction-rate probe into libhm_probe.so."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *CFLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("probe build failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print("built", PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

@@ -95,6 +95,10 @@ hm_status mixer_prefill_impl(const hm_prefill_args* a, hipStream_t stream, bool 
   HM_REQUIRE(a->ya != a->ys && a->ya != a->out && a->ys != a->out, HM_ERR_INVALID,
              "ya, ys and out must be distinct buffers");
   HM_REQUIRE(!a->kv_reuse || a->kv != nullptr, HM_ERR_INVALID, "kv_reuse needs a kv buffer");
+  if (a->events != nullptr) {
+    HM_REQUIRE(hm::prefill_fusable(a), HM_ERR_UNSUPPORTED,
+               "timing events are recorded by the bf16 one-stream launch sequence only");
+  }
   const bool cached_meta = a->meta_k != nullptr || a->meta_v != nullptr;
   if (cached_meta) {
     HM_PTR(a->meta_k);

@@ -179,6 +179,15 @@ hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, 
   float* S = E + (size_t)B * nC * kNS * Di;
   const int gx = (Di + 63) / 64;
 
+  // caller's timing events around the three launches (optional)
+  auto mark = [&](int i) -> hm_status {
+    if (a->events == nullptr || a->events[i] == nullptr) return HM_OK;
+    if (hipEventRecord((hipEvent_t)a->events[i], st) != hipSuccess)
+      return fail(HM_ERR_HIP, "hipEventRecord of a timing event failed");
+    return HM_OK;
+  };
+  hm_status s = mark(0);
+  if (s != HM_OK) return s;
   // 1. K/V pre-pass | chunk aggregates (chunks 0 .. nC-2)
   PrepGeom pg{a->kv_reuse ? 0 : (Tpad / 16) * Hkv * B, Tpad / 16, Hkv, Mk,
               (const bf16_t*)a->meta_k, (const bf16_t*)a->meta_v};
@@ -189,9 +198,11 @@ hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, 
                        ag, (const bf16_t*)a->x, (const bf16_t*)a->delta, a->A,
                        (const bf16_t*)a->Bm, a->conv_w, a->conv_b, a->conv_state_in, E, S, T,
                        Di, L, nC);
-    hm_status s = check_launch("prefill_prep_agg");
+    s = check_launch("prefill_prep_agg");
     if (s != HM_OK) return s;
   }
+  s = mark(1);
+  if (s != HM_OK) return s;
   // 2. attention | final scan pass
   const int n_qt = (T + kBM - 1) / kBM;          // query tiles over the token rows
   const int n_groups = B * Hkv * n_qt;
@@ -205,11 +216,15 @@ hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, 
                      (const bf16_t*)a->Bm, (const bf16_t*)a->Cm, a->D, (const bf16_t*)a->z,
                      a->conv_w, a->conv_b, a->conv_state_in, a->conv_state_out, a->h0, E, S,
                      (bf16_t*)a->ys, a->h_out, T, Di, L, nC, Mk);
-  hm_status s = check_launch("prefill_attn_final");
+  s = check_launch("prefill_attn_final");
+  if (s != HM_OK) return s;
+  s = mark(2);
   if (s != HM_OK) return s;
   // 3. branch norm and average
-  return norm_mean_impl(a->ya, a->ys, a->beta_a, a->beta_s, a->eps, a->out, (long long)B * T, Di,
-                        a->dtype, st, /*dry=*/false);
+  s = norm_mean_impl(a->ya, a->ys, a->beta_a, a->beta_s, a->eps, a->out, (long long)B * T, Di,
+                     a->dtype, st, /*dry=*/false);
+  if (s != HM_OK) return s;
+  return mark(3);
 }
 
 }  // namespace hm

@@ -55,9 +55,15 @@ class StackPlan:
                 kvs[i] = p.kv
             self.plans.append(p)
 
-    def run(self):
-        for p in self.plans:
-            p.run()
+    def run(self, events=None):
+        """events: optional per-layer lists of 4 timing events (see
+        PrefillPlan.run)."""
+        if events is None:
+            for p in self.plans:
+                p.run()
+        else:
+            for p, ev in zip(self.plans, events):
+                p.run(events=ev)
 
 
 class BlockStack:

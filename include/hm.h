@@ -244,6 +244,12 @@ hm_status hm_rms_norm(const void* x, const float* w, float eps, void* out, long 
  * covers n_meta + T rows: hm_attn_kv_bytes(B, n_meta + T, Hkv, Dh, dtype).
  * Supported for bf16 with Dh = 64 on one stream (no stream2); otherwise
  * HM_ERR_UNSUPPORTED.
+ * Timing (optional): events points to 4 caller-created hipEvent_t (as void*)
+ * that the bf16 one-stream sequence records on `stream` before its first
+ * launch, between the launches and after the last, so that the caller can
+ * time each of the three kernels with hipEventElapsedTime; NULL entries are
+ * skipped.  Other layer modes (stream2, float32) return HM_ERR_UNSUPPORTED
+ * when events is set.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int B, T, Hq, Hkv, Dh, Di, N, K, n_meta, window;
@@ -264,6 +270,7 @@ typedef struct {
   size_t workspace_bytes;
   const void *meta_k, *meta_v;                /* optional [n_meta, Hkv, Dh], see below */
   const float *conv_state_in, *h0;            /* optional [B, Di, K-1], [B, Di, N] */
+  void* const* events;                        /* optional HOST array of 4 hipEvent_t */
 } hm_prefill_args;
 hm_status hm_mixer_prefill(const hm_prefill_args* a, void* stream);
 size_t hm_mixer_prefill_workspace(const hm_prefill_args* a);
