@@ -321,8 +321,11 @@ def cpu_baseline_decode(shape, runs: int = 3):
 def alu_probe(hm_dir: str):
     """Measured instruction rates of the vector ALU (libhm_probe.so): the
     transcendental rate, the fused multiply-add rate and the selective scan's
-    single-pass mix (20 transcendental + 77 other VALU per token-channel), each
-    over 2048 workgroups of 256 lanes (8 waves per SIMD) timed with HIP events."""
+    single-pass mix (20 transcendental + 77 other VALU per token-channel), over
+    the whole chip (2048 workgroups of 256 lanes, 8 waves per SIMD) timed with
+    HIP events; and per SIMD at 1, 2, 4 and 8 waves, in shader-clock cycles
+    (s_memtime against the 100 MHz s_memrealtime), which gives the clock the
+    waves ran at and the issue rate per SIMD per cycle."""
     import ctypes
     import torch
     path = os.path.join(hm_dir, "libhm_probe.so")
@@ -330,27 +333,51 @@ def alu_probe(hm_dir: str):
         return None
     lib = ctypes.CDLL(path)
     lib.hm_probe_alu.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                 ctypes.c_void_p]
+                                 ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.hm_probe_alu_counts.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                         ctypes.POINTER(ctypes.c_int)]
+    res = {}
+    modes = ((0, "exp", 4000), (1, "fma", 4000), (2, "scan_mix", 60))
+    # whole chip, 8 waves per SIMD
     blocks = 2048
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
-    res = {}
-    for mode, name, iters in ((0, "exp", 4000), (1, "fma", 4000), (2, "scan_mix", 60)):
+    clk = torch.zeros(2 * blocks * 4, dtype=torch.int64, device="cuda")
+    for mode, name, iters in modes:
         st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        call = lambda: lib.hm_probe_alu(mode, ctypes.c_void_p(out.data_ptr()), blocks, iters, st)
+        call = lambda: lib.hm_probe_alu(mode, ctypes.c_void_p(out.data_ptr()), blocks, 256,
+                                        iters, ctypes.c_void_p(clk.data_ptr()), st)
         assert call() == 0
         ms = timed(call, 5, 2)
+        c = clk.view(-1, 2).double()
+        ghz = float((c[:, 0] / (c[:, 1] / 100e6)).median()) / 1e9
         tr, va = ctypes.c_int(), ctypes.c_int()
         lib.hm_probe_alu_counts(mode, ctypes.byref(tr), ctypes.byref(va))
         lanes = blocks * 256 * iters
         res[name] = {"trans_lane_ops_per_s": lanes * tr.value / (ms * 1e-3),
-                     "valu_lane_ops_per_s": lanes * va.value / (ms * 1e-3), "ms": ms}
+                     "valu_lane_ops_per_s": lanes * va.value / (ms * 1e-3), "ms": ms,
+                     "clock_ghz": ghz}
     # the scan mix: 8 token-channels per lane per iteration
     res["scan_mix"]["token_channels_per_s"] = blocks * 256 * 60 * 8 / (res["scan_mix"]["ms"] * 1e-3)
-    res["note"] = ("lane-ops/s over the chip; 256 CUs x 64 lanes x 2.4 GHz = 3.93e13 is the "
-                   "nominal non-packed fp32 rate; the scan mix is run as written, so its "
-                   "token-channels/s is the ALU ceiling of a single-pass scan")
+    # per SIMD: one workgroup of w waves per CU... w waves on each SIMD of every CU:
+    # 256 x 4 x w waves in 256-lane workgroups
+    per_simd = {}
+    for mode, name, iters in modes[:2]:
+        for w in (1, 2, 4, 8):
+            nb = 256 * w
+            o = torch.empty(nb * 256, dtype=torch.float32, device="cuda")
+            ck = torch.zeros(2 * nb * 4, dtype=torch.int64, device="cuda")
+            st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            assert lib.hm_probe_alu(mode, ctypes.c_void_p(o.data_ptr()), nb, 256, iters,
+                                    ctypes.c_void_p(ck.data_ptr()), st) == 0
+            torch.cuda.synchronize()
+            c = ck.view(-1, 2).double()
+            cyc = float(c[:, 0].median())
+            # instructions one wave issues / its cycles x waves sharing the SIMD
+            per_simd[f"{name}_w{w}"] = {"instr_per_cycle_per_simd": 8 * iters * w / cyc,
+                                        "clock_ghz": float((c[:, 0] / (c[:, 1] / 100e6)).median()) / 1e9}
+    res["per_simd"] = per_simd
+    res["note"] = ("chip rates in lane-ops/s; per_simd: wave64 instructions issued per shader "
+                   "cycle per SIMD with w waves on every SIMD (median wave), from s_memtime")
     return res
 
 

@@ -664,10 +664,15 @@ hm_status hm_debug_step_positions(int B, long long n_prev, const int* n_prev_seq
 
 namespace {
 
-// The decode step with its scratch memory given explicitly (ws, ws_bytes):
-// the caller's workspace (hm_mixer_step) or the library's static scratch
-// array (hm_mixer_step_noalloc).  a->workspace is not read here.
-hm_status mixer_step_impl(const hm_step_args* a, void* ws, size_t ws_bytes, void* stream) {
+hm_status step_scratch_ptr(void** out);
+constexpr size_t kStepScratchBytes = (size_t)8 << 20;
+
+// The decode step with its scratch memory given explicitly (ws, ws_bytes): the
+// caller's workspace (hm_mixer_step), or, with use_scratch, the library's
+// static scratch array (hm_mixer_step_noalloc), looked up only once every
+// argument has been validated.  a->workspace is not read here.
+hm_status mixer_step_impl(const hm_step_args* a, void* ws, size_t ws_bytes, void* stream,
+                          bool use_scratch) {
   HM_REQUIRE(a != nullptr, HM_ERR_INVALID, "args is NULL");
   HM_REQUIRE(a->B > 0 && a->Hq > 0 && a->Hkv > 0 && a->Dh > 0 && a->Di > 0, HM_ERR_INVALID,
              "B, Hq, Hkv, Dh and Di must be positive");
@@ -728,6 +733,15 @@ hm_status mixer_step_impl(const hm_step_args* a, void* ws, size_t ws_bytes, void
   const size_t need = g.ys_bytes + g.part_bytes;
   HM_REQUIRE((size_t)a->Hq * g.n_split <= (size_t)kCombMaxW, HM_ERR_UNSUPPORTED,
              "too many query heads x key splits for the combine");
+  if (use_scratch) {
+    HM_REQUIRE(need <= kStepScratchBytes, HM_ERR_UNSUPPORTED,
+               "step needs " + std::to_string(need) + " bytes of scratch, more than the " +
+                   std::to_string(kStepScratchBytes) +
+                   " of the allocation-free entry point; use hm_mixer_step with a workspace");
+    hm_status s = step_scratch_ptr(&ws);
+    if (s != HM_OK) return s;
+    ws_bytes = kStepScratchBytes;
+  }
   HM_REQUIRE(ws != nullptr && ws_bytes >= need && hm::aligned16(ws), HM_ERR_WORKSPACE,
              "workspace smaller than hm_mixer_step_workspace()");
 
@@ -797,7 +811,6 @@ hm_status mixer_step_impl(const hm_step_args* a, void* ws, size_t ws_bytes, void
 // itself (on the host it is only a stand-in for the symbol): its device
 // address is looked up once per device with hipGetSymbolAddress and that
 // address is what the kernels receive.
-constexpr size_t kStepScratchBytes = (size_t)8 << 20;
 static __device__ __align__(256) unsigned char step_scratch[kStepScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -832,22 +845,13 @@ extern "C" {
 
 hm_status hm_mixer_step(const hm_step_args* a, void* stream) {
   HM_REQUIRE(a != nullptr, HM_ERR_INVALID, "args is NULL");
-  return mixer_step_impl(a, a->workspace, a->workspace_bytes, stream);
+  return mixer_step_impl(a, a->workspace, a->workspace_bytes, stream, false);
 }
 
 size_t hm_mixer_step_noalloc_max_bytes(void) { return kStepScratchBytes; }
 
 hm_status hm_mixer_step_noalloc(const hm_step_args* a, void* stream) {
-  HM_REQUIRE(a != nullptr, HM_ERR_INVALID, "args is NULL");
-  const size_t need = hm_mixer_step_workspace(a);
-  HM_REQUIRE(need <= kStepScratchBytes, HM_ERR_UNSUPPORTED,
-             "step needs " + std::to_string(need) + " bytes of scratch, more than the " +
-                 std::to_string(kStepScratchBytes) +
-                 " of the allocation-free entry point; use hm_mixer_step with a workspace");
-  void* ws = nullptr;
-  hm_status s = step_scratch_ptr(&ws);
-  if (s != HM_OK) return s;
-  return mixer_step_impl(a, ws, kStepScratchBytes, stream);
+  return mixer_step_impl(a, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

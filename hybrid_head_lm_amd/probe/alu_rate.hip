@@ -26,7 +26,12 @@ __device__ __forceinline__ float vfma(float x, float a, float b) {
 
 template <int MODE>
 __global__ __launch_bounds__(256) void alu_probe(float* __restrict__ out, int iters, float a,
-                                                 float b) {
+                                                 float b, long long* __restrict__ clk) {
+  // shader-clock cycles (s_memtime) and 100 MHz ticks (s_memrealtime) around
+  // the loop, recorded by lane 0 of each wave: their ratio is the clock the
+  // wave ran at
+  const long long c0 = __builtin_amdgcn_s_memtime();
+  const long long r0 = __builtin_amdgcn_s_memrealtime();
   float x[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = 0.25f + 0.01f * (float)(threadIdx.x & 7) + 0.001f * i;
@@ -54,7 +59,14 @@ __global__ __launch_bounds__(256) void alu_probe(float* __restrict__ out, int it
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) s += x[i];
-  out[blockIdx.x * 256 + threadIdx.x] = s;
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+  const long long c1 = __builtin_amdgcn_s_memtime();
+  const long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (clk != nullptr && (threadIdx.x & 63) == 0) {
+    const int w = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    clk[2 * w] = c1 - c0;
+    clk[2 * w + 1] = r1 - r0;
+  }
 }
 
 }  // namespace
@@ -67,17 +79,23 @@ void hm_probe_alu_counts(int mode, int* trans, int* valu) {
   *valu = mode == 0 ? 0 : (mode == 1 ? 8 : 8 * 77);
 }
 
-// Launch `blocks` workgroups of 256 lanes, each running `iters` iterations of
-// `mode`; out: device float [blocks * 256].  Returns 0 on success.
-int hm_probe_alu(int mode, float* out, int blocks, int iters, void* stream) {
-  if (out == nullptr || blocks <= 0 || iters <= 0 || mode < 0 || mode > 2) return 1;
+// Launch `blocks` workgroups of `threads` lanes (a multiple of 64, at most
+// 256), each running `iters` iterations of `mode`; out: device float
+// [blocks * threads]; clk: device int64 [2 * blocks * threads / 64] or NULL
+// (per wave: shader cycles, 100 MHz ticks).  Returns 0 on success.
+int hm_probe_alu(int mode, float* out, int blocks, int threads, int iters, long long* clk,
+                 void* stream) {
+  if (out == nullptr || blocks <= 0 || iters <= 0 || mode < 0 || mode > 2 || threads < 64 ||
+      threads > 256 || threads % 64 != 0)
+    return 1;
   hipStream_t st = (hipStream_t)stream;
+  const dim3 g(blocks), t(threads);
   if (mode == 0)
-    hipLaunchKernelGGL(alu_probe<0>, dim3(blocks), dim3(256), 0, st, out, iters, 0.999f, 0.001f);
+    hipLaunchKernelGGL(alu_probe<0>, g, t, 0, st, out, iters, 0.999f, 0.001f, clk);
   else if (mode == 1)
-    hipLaunchKernelGGL(alu_probe<1>, dim3(blocks), dim3(256), 0, st, out, iters, 0.999f, 0.001f);
+    hipLaunchKernelGGL(alu_probe<1>, g, t, 0, st, out, iters, 0.999f, 0.001f, clk);
   else
-    hipLaunchKernelGGL(alu_probe<2>, dim3(blocks), dim3(256), 0, st, out, iters, 0.999f, 0.001f);
+    hipLaunchKernelGGL(alu_probe<2>, g, t, 0, st, out, iters, 0.999f, 0.001f, clk);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
