@@ -218,10 +218,20 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
     float* __restrict__ conv_state, float* __restrict__ ssm_state, float* __restrict__ ys_ws,
     size_t ys_stride, float* __restrict__ part, size_t part_b_stride, int Hq, int Hkv, int Di,
     int S, SeqPos sp, float qscale, double log2_base, double rstep,
-    int n_split, int tiles_per_split, int ssm_per_block, int n_ssm) {
+    int n_split, int tiles_per_split, int ssm_per_block, int n_ssm, int n_attn) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecStages][2][8192];
   __shared__ float sm[4][16], sl[4][16];
   const int tid = threadIdx.x;
+  if ((int)blockIdx.x >= n_attn) {
+    // workgroups past the attention ones run SSM-step items only
+    const int nb = (int)gridDim.x - n_attn;
+    for (int j = ((int)blockIdx.x - n_attn) * 256 + tid; j < n_ssm; j += nb * 256) {
+      const int bs = j / Di, c = j % Di;
+      ys_ws[(size_t)bs * ys_stride + c] =
+          ssm_step_one<bf16_t>(bs, c, Di, x, dl, Bm, Cm, z, A, D, cw, cb, conv_state, ssm_state);
+    }
+    return;
+  }
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, G = lane >> 4;
   const int grp = Hq / Hkv;
@@ -603,6 +613,11 @@ struct StepGeom {
 // bf16 decode: key splits of whole 64-row tiles, about kDecBlocks workgroups
 // in all (two to three per CU stream at once with 48 KB of LDS each).
 constexpr int kDecBlocks = 640;
+// SSM-step items per thread of the workgroups that run only the SSM step
+// (measured: 1 item per thread in workgroups of their own beats a share of
+// every attention workgroup, which kept the stream's tail waiting on the
+// exponentials; 0 selects that shared form)
+constexpr int kSsmItems = 1;
 
 StepGeom step_geom(const hm_step_args* a) {
   StepGeom s{};
@@ -756,15 +771,18 @@ hm_status mixer_step_impl(const hm_step_args* a, void* ws, size_t ws_bytes, void
   if (a->dtype == HM_BF16) {
     const int n_attn = a->B * a->Hkv * g.n_split;
     const int n_ssm = a->B * a->Di;
-    const int ssm_per_block = (n_ssm + n_attn - 1) / n_attn;
-    hipLaunchKernelGGL(step_fused_bf16, dim3(n_attn), dim3(256), 0, st,
+    // SSM-step items: a share of every attention workgroup, or (kSsmItems > 0)
+    // workgroups of their own with kSsmItems items per thread
+    const int ssm_per_block = kSsmItems > 0 ? 0 : (n_ssm + n_attn - 1) / n_attn;
+    const int n_ssm_blocks = kSsmItems > 0 ? (n_ssm + 256 * kSsmItems - 1) / (256 * kSsmItems) : 0;
+    hipLaunchKernelGGL(step_fused_bf16, dim3(n_attn + n_ssm_blocks), dim3(256), 0, st,
                        (const bf16_t*)a->q, (const bf16_t*)a->k_new, (const bf16_t*)a->v_new,
                        (bf16_t*)a->k_cache, (bf16_t*)a->v_cache, (const bf16_t*)a->x,
                        (const bf16_t*)a->delta, (const bf16_t*)a->Bm, (const bf16_t*)a->Cm,
                        (const bf16_t*)a->z, a->A, a->D, a->conv_w, a->conv_b, a->conv_state,
                        a->ssm_state, ys_ws, g.ys_stride, part, g.part_b_stride, a->Hq, a->Hkv,
                        a->Di, S, sp, sc, l2b, exp2(-l2b / 32.0), g.n_split,
-                       g.tiles_per_split, ssm_per_block, n_ssm);
+                       g.tiles_per_split, ssm_per_block, n_ssm, n_attn);
     hm_status s = hm::check_launch("step_fused_bf16");
     if (s != HM_OK) return s;
     hipLaunchKernelGGL(step_combine<bf16_t>, dim3(a->B), dim3(kCombThreads), 0, st,
