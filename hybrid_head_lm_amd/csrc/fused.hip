@@ -155,47 +155,6 @@ prefill_attn_final(int n_attn, const bf16_t* __restrict__ q, const bf16_t* __res
 
 namespace hm {
 
-// The conv + scan branch alone in two launches (bf16, 16-byte aligned rows):
-// the chunk aggregates, then the final pass with each workgroup composing its
-// own incoming states (no carry launch).  The same kernels as a prefill layer,
-// with no K/V pre-pass and no attention range.
-bool conv_scan_two_launch_ok(const void* x, const void* delta, const void* Bm, const void* Cm,
-                             const void* z, int Di) {
-  return Di % 8 == 0 && aligned16(x) && aligned16(delta) && aligned16(Bm) && aligned16(Cm) &&
-         (z == nullptr || aligned16(z));
-}
-
-hm_status conv_scan_two_launch_bf16(const void* x, const float* cw, const float* cb,
-                                    const float* cst_in, float* cst_out, const void* delta,
-                                    const float* A, const void* Bm, const void* Cm,
-                                    const float* D, const void* z, const float* h0, void* y,
-                                    float* h_out, int B, int T, int Di, void* scan_ws,
-                                    hipStream_t st) {
-  const int L = scan_chunk_len(B, T, Di);
-  const int nC = (T + L - 1) / L;
-  float* E = (float*)scan_ws;
-  float* S = E + (size_t)B * nC * kNS * Di;
-  const int gx = (Di + 63) / 64;
-  const PrepGeom pg{0, 1, 1, 0, nullptr, nullptr};
-  const AggGeom ag{gx * (nC - 1) * B, gx, nC > 1 ? nC - 1 : 1};
-  if (ag.n > 0) {
-    hipLaunchKernelGGL(prefill_prep_agg, dim3(ag.n), dim3(64), 0, st, pg, nullptr, nullptr,
-                       nullptr, nullptr, 64, 0LL, 1.0, ag, (const bf16_t*)x,
-                       (const bf16_t*)delta, A, (const bf16_t*)Bm, cw, cb, cst_in, E, S, T, Di, L,
-                       nC);
-    hm_status s = check_launch("prefill_prep_agg (scan aggregates)");
-    if (s != HM_OK) return s;
-  }
-  const FinalGeom fg{gx, (nC + kChunkWaves - 1) / kChunkWaves};
-  const int n_final = fg.gx * fg.nJ * B;
-  hipLaunchKernelGGL(prefill_attn_final, dim3(n_final), dim3(256), 0, st, 0, nullptr, nullptr,
-                     nullptr, nullptr, 64, 1, 1, 0, 0, 0LL, 0.f, 1.0, 1, 1, fg,
-                     (const bf16_t*)x, (const bf16_t*)delta, A, (const bf16_t*)Bm,
-                     (const bf16_t*)Cm, D, (const bf16_t*)z, cw, cb, cst_in, cst_out, h0, E, S,
-                     (bf16_t*)y, h_out, T, Di, L, nC, 0);
-  return check_launch("prefill_attn_final (scan final pass)");
-}
-
 bool prefill_fusable(const hm_prefill_args* a) {
   return a->dtype == HM_BF16 && a->stream2 == nullptr && a->Dh == 64 && a->N == kNS &&
          a->K == kConvK && a->Di % 8 == 0 && aligned16(a->x) && aligned16(a->delta) &&

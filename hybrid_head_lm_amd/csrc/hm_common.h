@@ -175,16 +175,6 @@ hm_status conv_scan_impl(const void* x, const float* conv_w, const float* conv_b
                          float* h_out, int B, int T, int Di, int K, int N, hm_dtype dtype,
                          void* workspace, size_t workspace_bytes, hipStream_t st,
                          bool fuse_conv, bool dry);
-// The conv + scan branch in two launches (fused.hip): bf16 with the conv fused,
-// rows and bases 16-byte aligned; the caller has validated every argument.
-bool conv_scan_two_launch_ok(const void* x, const void* delta, const void* Bm, const void* Cm,
-                             const void* z, int Di);
-hm_status conv_scan_two_launch_bf16(const void* x, const float* cw, const float* cb,
-                                    const float* cst_in, float* cst_out, const void* delta,
-                                    const float* A, const void* Bm, const void* Cm,
-                                    const float* D, const void* z, const float* h0, void* y,
-                                    float* h_out, int B, int T, int Di, void* scan_ws,
-                                    hipStream_t st);
 // Fused launch sequence of a bf16 prefill layer (fused.hip); the caller has
 // validated every argument.
 bool prefill_fusable(const hm_prefill_args* a);
