@@ -102,10 +102,11 @@ __global__ __launch_bounds__(256) void norm_mean_vec(const Tact* __restrict__ ya
   }
 }
 
-// width % 8 == 0 and width <= 64 * 8 * kMaxC: eight rows per workgroup (one per
-// wave), each row held in registers; the two beta vectors are staged in LDS
-// once per workgroup instead of being read by every wave.
-constexpr int kRowsPerBlock = 8;
+// width % 8 == 0 and width <= 64 * 8 * kMaxC: four rows per workgroup (one per
+// wave; measured a little faster than eight at 33 024 rows), each row held in
+// registers; the two beta vectors are staged in LDS once per workgroup instead
+// of being read by every wave.
+constexpr int kRowsPerBlock = 4;
 
 template <typename Tact>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void norm_mean_rows(
@@ -212,7 +213,7 @@ void launch_norm(const void* ya, const void* ys, const float* ba, const float* b
 
 // RMS norm with a learned weight (the block's two normalisation layers):
 // out = x / sqrt(mean(x^2) + eps) * w per row.  width % 8 == 0 and width <=
-// 64 * 8 * kMaxC: eight rows per workgroup, one per wave, held in registers;
+// 64 * 8 * kMaxC: four rows per workgroup, one per wave, held in registers;
 // the weight is staged in LDS once per workgroup.
 template <typename Tact>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void rms_norm_rows(

@@ -273,6 +273,33 @@ def test_mixer_prefill_kv_reuse_one_stream():
             assert_close(down(got), ref[k], "bf16", k)
 
 
+# ------------------------------------------------------------------ timing events
+def test_mixer_prefill_events_leave_results_unchanged():
+    """The optional events are recorded between the fused launches and change
+    nothing else: outputs bit-identical to a run without them, the recorded
+    intervals non-negative, and a NULL entry skipped."""
+    shape = with_(SWA_PREFILL, N=600, M=32, W=128)
+    t = up_inputs(prefill_inputs(shape, 31), "bf16")
+    plan = hm.PrefillPlan(t, shape.M, shape.W)
+    plan.run()
+    torch.cuda.synchronize()
+    base = {k: getattr(plan, k).clone() for k in ("ya", "ys", "out", "h")}
+    for skip in (None, 2):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in evs:
+            e.record()
+        torch.cuda.synchronize()
+        use = [None if i == skip else e for i, e in enumerate(evs)]
+        plan.run(events=use)
+        torch.cuda.synchronize()
+        for k, ref in base.items():
+            assert torch.equal(getattr(plan, k), ref), k
+        live = [e for e in use if e is not None]
+        gaps = [a.elapsed_time(b) for a, b in zip(live, live[1:])]
+        assert all(g >= 0 for g in gaps), gaps
+        assert live[0].elapsed_time(live[-1]) > 0
+
+
 # ------------------------------------------------------------------ prepared K/V, two streams
 def test_prepared_kv_shared_between_layers():
     shape = with_(SWA_PREFILL, N=500, M=16, W=128)
