@@ -9,7 +9,8 @@
 // stages (one workgroup per CU); LDS rows are 128 bytes with the 16-byte chunk
 // c of row r in slot c ^ ((r >> 1) & 7), so the 16 lanes of an operand read
 // (16 consecutive rows, one chunk) hit 16 different bank groups.  Tiles are
-// dealt to the XCDs in contiguous ranges (workgroup b runs on XCD b % 8).
+// dealt to the XCDs in contiguous ranges (workgroup b runs on XCD b % 8), in
+// groups of 4 tile rows.
 // The finished tile leaves through LDS in two halves of 128 rows as 16-byte
 // row chunks, the residual added after the activation.
 #include "linear_dev.h"
@@ -19,6 +20,7 @@ namespace {
 using namespace hm_lin;
 
 constexpr int kTM = 256, kTN = 256, kTK = 64;
+constexpr int kGroupM = 4;
 
 HM_DEV int w4_off(int row, int c) { return row * 128 + ((c ^ ((row >> 1) & 7)) << 4); }
 
@@ -32,7 +34,14 @@ __global__ __launch_bounds__(256) void linear_bf16_w4(const bf16_t* __restrict__
   if (t >= tiles_m * tiles_n) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int m0 = (t / tiles_n) * kTM, n0 = (t % tiles_n) * kTN;
+  // Grouped order inside an XCD's range: groups of kGroupM tile rows are walked
+  // column by column, so that the 32 tiles an XCD runs at once cover 4 rows x 8
+  // columns (12 operand panels in its L2 instead of ~23 for row-major order).
+  // Measured on the block's shapes: fetched bytes 2.1 -> 1.0 GB (in-projection)
+  // and 4.7 -> 1.9 GB (FFN up), 2-5% faster.
+  const int gsz = kGroupM * tiles_n, grp0 = (t / gsz) * kGroupM;
+  const int gm = min(kGroupM, tiles_m - grp0), tl = t % gsz;
+  const int m0 = (grp0 + tl % gm) * kTM, n0 = (tl / gm) * kTN;
 
   // This thread's 16-byte chunks of each K step: wave v fills LDS rows
   // 64 v .. 64 v + 63 of x's and of W's tile, 8 rows per instruction, lane L
