@@ -6,7 +6,9 @@
 //   rms(y) = sqrt(mean(y^2) + eps) over the whole branch width of a token.
 // One wave per row: both sums of squares in float32 (16-byte loads), a wave
 // reduction, then the output row.  HBM traffic: read ya and ys once, write out.
+#include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "hm_common.h"
 
@@ -166,6 +168,90 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void norm_mean_rows(
   }
 }
 
+// bf16 rows (width % 8 == 0, width <= 64 * 8 * kMaxC): one row per wave,
+// held packed in registers (16 bytes per chunk, 32 VGPRs for both branches)
+// and unpacked twice (sums of squares, output), so that six waves fit a SIMD
+// (the float copy of the row in norm_mean_rows allows five).  The two beta
+// vectors are staged in LDS once per workgroup and read from there per chunk.
+// Measured at 33 024 rows of 1600: 53 us (6.0 TB/s) against 70 us.  The row
+// loop strides over the grid, which the launch sizes to one row per wave.
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6, 6))) void norm_mean_rows_bf16(
+    const bf16_t* __restrict__ ya, const bf16_t* __restrict__ ys, const float* __restrict__ ba,
+    const float* __restrict__ bs, float eps, bf16_t* __restrict__ out, long long rows,
+    int width) {
+  __shared__ float4 sb[2][64 * kMaxC * 2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n8 = width >> 3;
+  for (int i = threadIdx.x; i < 2 * n8; i += 256) {
+    sb[0][i] = ((const float4*)ba)[i];
+    sb[1][i] = ((const float4*)bs)[i];
+  }
+  __syncthreads();
+  const float inv_w = 1.f / (float)width;
+  for (long long row = (long long)blockIdx.x * 4 + wave; row < rows;
+       row += (long long)gridDim.x * 4) {
+    // beta is read from LDS per row: kept out of registers (64 of them per
+    // lane would halve the waves per SIMD)
+    __asm__ volatile("" ::: "memory");
+    const bf16_t* pa = ya + row * width;
+    const bf16_t* ps = ys + row * width;
+    uint4 a[kMaxC], sv[kMaxC];
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k) {
+      const int c = min(lane + 64 * k, n8 - 1);   // clamped: every load unconditional
+      a[k] = *(const uint4*)(pa + 8 * c);
+      sv[k] = *(const uint4*)(ps + 8 * c);
+    }
+    float sa = 0.f, ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k)
+      if (lane + 64 * k < n8) {
+        const uint32_t wa[4] = {a[k].x, a[k].y, a[k].z, a[k].w};
+        const uint32_t ws[4] = {sv[k].x, sv[k].y, sv[k].z, sv[k].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a0 = __uint_as_float(wa[i] << 16), a1 = __uint_as_float(wa[i] & 0xffff0000u);
+          const float s0 = __uint_as_float(ws[i] << 16), s1 = __uint_as_float(ws[i] & 0xffff0000u);
+          sa = fmaf(a0, a0, fmaf(a1, a1, sa));
+          ss = fmaf(s0, s0, fmaf(s1, s1, ss));
+        }
+      }
+    // the row is unpacked again for the output (not kept as 64 floats)
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k)
+      __asm__ volatile("" : "+v"(a[k].x), "+v"(a[k].y), "+v"(a[k].z), "+v"(a[k].w),
+                       "+v"(sv[k].x), "+v"(sv[k].y), "+v"(sv[k].z), "+v"(sv[k].w));
+    sa = wave_sum(sa);
+    ss = wave_sum(ss);
+    const float ra = 0.5f / sqrtf(sa * inv_w + eps);
+    const float rs = 0.5f / sqrtf(ss * inv_w + eps);
+    bf16_t* po = out + row * width;
+#pragma unroll
+    for (int k = 0; k < kMaxC; ++k) {
+      const int c = lane + 64 * k;
+      if (c < n8) {
+        const float4 b0 = sb[0][2 * c], b1 = sb[0][2 * c + 1];
+        const float4 c0 = sb[1][2 * c], c1 = sb[1][2 * c + 1];
+        const float w1[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const float w2[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const uint32_t wa[4] = {a[k].x, a[k].y, a[k].z, a[k].w};
+        const uint32_t ws[4] = {sv[k].x, sv[k].y, sv[k].z, sv[k].w};
+        float r[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          r[2 * i] = w1[2 * i] * __uint_as_float(wa[i] << 16) * ra +
+                     w2[2 * i] * __uint_as_float(ws[i] << 16) * rs;
+          r[2 * i + 1] = w1[2 * i + 1] * __uint_as_float(wa[i] & 0xffff0000u) * ra +
+                         w2[2 * i + 1] * __uint_as_float(ws[i] & 0xffff0000u) * rs;
+        }
+        Vec8<bf16_t>::st(po + 8 * c, r);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one chunk's beta in registers at a time
+    }
+  }
+}
+
 // any width
 template <typename Tact>
 __global__ __launch_bounds__(256) void norm_mean_scalar(const Tact* __restrict__ ya,
@@ -198,7 +284,12 @@ template <typename Tact>
 void launch_norm(const void* ya, const void* ys, const float* ba, const float* bs, float eps,
                  void* out, long long rows, int width, hipStream_t st) {
   const dim3 grid((unsigned)((rows + 3) / 4));
-  if (width % 8 == 0 && width <= 64 * 8 * kMaxC)
+  if (std::is_same<Tact, bf16_t>::value && width % 8 == 0 && width <= 64 * 8 * kMaxC) {
+    const long long g = std::min<long long>((rows + 3) / 4, 1ll << 30);
+    hipLaunchKernelGGL(norm_mean_rows_bf16, dim3((unsigned)g), dim3(256), 0, st,
+                       (const bf16_t*)ya, (const bf16_t*)ys, ba, bs, eps, (bf16_t*)out, rows,
+                       width);
+  } else if (width % 8 == 0 && width <= 64 * 8 * kMaxC)
     hipLaunchKernelGGL(norm_mean_rows<Tact>, dim3((unsigned)((rows + kRowsPerBlock - 1) /
                                                             kRowsPerBlock)),
                        dim3(64 * kRowsPerBlock), 0, st, (const Tact*)ya, (const Tact*)ys, ba, bs,
