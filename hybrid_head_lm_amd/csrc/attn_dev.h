@@ -155,6 +155,12 @@ HM_DEV void attn_fwd_bf16_body(
   const int g = pair % Hkv, b = pair / Hkv;
   const int h = g * grp + hh;
 
+  // Attention waves issue at priority 2, 3 while their QK product is issued:
+  // in the fused prefill launch they share CUs with final-scan waves (priority
+  // 0), whose VALU work then fills the attention waves' idle issue slots
+  // instead of delaying their softmax (measured: the swa-prefill fused launch
+  // 48.7 -> 46.7 us).
+  __builtin_amdgcn_s_setprio(2);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 31, gq = lane >> 5;
@@ -263,7 +269,7 @@ HM_DEV void attn_fwd_bf16_body(
     // S^T - m_ref (accumulated onto -m_ref); the two 32-key blocks are
     // independent accumulation chains, alternated
     const unsigned char* sk = smem[it % kStages][0];
-    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_s_setprio(3);
     f32x16_v S[2];
     S[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8_v*)(sk + lds_off(n, gq)),
                                                    qf[0], cinit, 0, 0, 0);
@@ -275,7 +281,7 @@ HM_DEV void attn_fwd_bf16_body(
       for (int kb = 0; kb < 2; ++kb)
         S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             *(const bf16x8_v*)(sk + lds_off(kb * 32 + n, 2 * k4 + gq)), qf[k4], S[kb], 0, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(2);
     if (cls == 1 || j0 + kBN > Tk) {
       // element (kb, i) is key kbase + off with off = 32 kb + 16 (i / 8) + i % 8;
       // visible iff off <= a and (off < mm or off >= w)  (hm_visible, shifted)
