@@ -33,7 +33,9 @@ Also reported on the same JSON line:
                  one over the swa-prefill rows, 32 chained at the stack's size;
   cpu_baseline   the float64 CPU oracle on a bounded sample of the stack
                  (layers 0, 1, 2, 15, 30, 31), extrapolated, in the step's unit;
-  cpu_baseline_decode  the oracle's decode step through the pair.
+  cpu_baseline_decode  the oracle's decode step through the pair; swa_prefill and
+                 global_prefill carry their own cpu_baseline (the whole layer, median
+                 of 3; a sampled global layer, extrapolated).
 HBM traffic (`traffic`) comes from the committed rocprofv3 counter summaries in
 profiles/ (null once the kernel sources differ from those the counters were
 taken with); `--counters` is the run those summaries are taken over.
@@ -231,6 +233,75 @@ CPU_QUERY_BLOCK = 512      # the oracle attention's own query-block size
 CPU_SCAN_ROWS = 1024       # rows of the sequential scan timed per layer
 
 
+def _oracle_layer_estimate(shape, window, q, k, v, part, prm):
+    """Seconds of the oracle's prefill layer, from one 512-row query block of
+    its attention (plus the K rotation it does once per call) and conv + scan +
+    norm over the first CPU_SCAN_ROWS rows, extrapolated to all rows (the
+    oracle scores every key of a row and masks, so each query block costs the
+    same; the scan is sequential, linear in the rows)."""
+    import numpy as np
+    import oracle
+    T, B = shape.T, shape.B
+    n_blocks = -(-T // CPU_QUERY_BLOCK)
+    qrows = np.arange(T // 2, T // 2 + CPU_QUERY_BLOCK)
+    S = min(CPU_SCAN_ROWS, T)
+    t0 = time.perf_counter()
+    oracle.rope(k, np.arange(T), shape.rope_base)
+    t_rope = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    ya = oracle.attention(q, k, v, shape.M, window, shape.rope_base, rows=qrows)
+    t_blk = time.perf_counter() - t0 - t_rope
+    t0 = time.perf_counter()
+    xc, _ = oracle.causal_conv1d(part["x"], prm["conv_w"], prm["conv_b"], None, True)
+    ys, _ = oracle.selective_scan(xc, part["delta"], prm["A"], part["Bm"], part["Cm"],
+                                  prm["D"], part["z"])
+    t_ssm = time.perf_counter() - t0
+    nr = min(S, len(qrows))
+    t0 = time.perf_counter()
+    oracle.branch_norm_mean(ya.reshape(B, len(qrows), -1)[:, :nr], ys[:, :nr],
+                            prm["beta_a"], prm["beta_s"], shape.eps)
+    t_norm = time.perf_counter() - t0
+    return t_rope + n_blocks * max(t_blk, 0.0) + (T / S) * t_ssm + (T / nr) * t_norm
+
+
+def _baseline_record(value, unit, sample, **extra):
+    rec = {"value": value, "unit": unit, "cores": blas_threads() or 1,
+           "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+           "kind": "oracle", "sample": sample}
+    rec.update(extra)
+    return rec
+
+
+def cpu_baseline_layer(shape, inp, runs: int = 3):
+    """The oracle's whole prefill layer on the workload's own host inputs,
+    median of `runs` (small workloads)."""
+    import oracle
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.mixer_prefill(inp, shape.M, shape.W, rope_base=shape.rope_base, eps=shape.eps)
+        ts.append(time.perf_counter() - t0)
+    med = sorted(ts)[len(ts) // 2]
+    return _baseline_record(shape.B * shape.T / med, "tokens/s",
+                            f"{shape.name}: the whole layer, median of {runs} runs",
+                            seconds_per_layer=med)
+
+
+def cpu_baseline_layer_sampled(shape, inp):
+    """The oracle's prefill layer on a bounded sample of a large workload
+    (one query block and the first CPU_SCAN_ROWS rows), extrapolated."""
+    S = min(CPU_SCAN_ROWS, shape.T)
+    part = {n: inp[n][:, :S] for n in ("x", "delta", "Bm", "Cm", "z")}
+    t0 = time.perf_counter()
+    est = _oracle_layer_estimate(shape, shape.W, inp["q"], inp["k"], inp["v"], part, inp)
+    wall = time.perf_counter() - t0
+    return _baseline_record(
+        shape.B * shape.T / est, "tokens/s",
+        f"{shape.name}: the oracle attention over one {CPU_QUERY_BLOCK}-row query block plus "
+        f"its K rotation, and conv + scan + norm over the first {S} rows, extrapolated to "
+        f"{shape.T} rows; {wall:.1f} s of CPU work", seconds_per_layer_estimated=est)
+
+
 def cpu_baseline_stack(shape, layers, roles):
     """The oracle (float64 NumPy, as it stands) on a bounded sample of the
     32-layer stack, extrapolated to the whole stack.
@@ -244,11 +315,8 @@ def cpu_baseline_stack(shape, layers, roles):
     (conv + scan + norm).  Stack estimate = 3 x mean(global layers) + 29 x
     mean(window layers).  Inputs are the stack's own device tensors copied to
     the host (the same bytes the GPU read)."""
-    import numpy as np
-    import oracle
-    T, B = shape.T, shape.B
+    T = shape.T
     n_blocks = -(-T // CPU_QUERY_BLOCK)
-    qrows = np.arange(T // 2, T // 2 + CPU_QUERY_BLOCK)
     per_role = {"global": [], "window": []}
     t_all0 = time.perf_counter()
     for layer in CPU_STACK_LAYERS:
@@ -256,45 +324,25 @@ def cpu_baseline_stack(shape, layers, roles):
         t = layers[layer]
         q = _host(t["q"])
         k, v = _host(layers[src]["k"]), _host(layers[src]["v"])
-        S = CPU_SCAN_ROWS
-        part = {n: _host(t[n][:, :S]) for n in ("x", "delta", "Bm", "Cm", "z")}
+        part = {n: _host(t[n][:, :CPU_SCAN_ROWS]) for n in ("x", "delta", "Bm", "Cm", "z")}
         prm = {n: _host(t[n]) for n in ("A", "D", "conv_w", "conv_b", "beta_a", "beta_s")}
-        # the K rotation of one attention call
-        t0 = time.perf_counter()
-        oracle.rope(k, np.arange(T), shape.rope_base)
-        t_rope = time.perf_counter() - t0
-        # one query block: the call rotates all of K once, so subtract that
-        t0 = time.perf_counter()
-        ya = oracle.attention(q, k, v, shape.M, window, shape.rope_base, rows=qrows)
-        t_blk = time.perf_counter() - t0 - t_rope
-        t0 = time.perf_counter()
-        xc, _ = oracle.causal_conv1d(part["x"], prm["conv_w"], prm["conv_b"], None, True)
-        ys, _ = oracle.selective_scan(xc, part["delta"], prm["A"], part["Bm"], part["Cm"],
-                                      prm["D"], part["z"])
-        t_ssm = time.perf_counter() - t0
-        nr = min(S, len(qrows))
-        t0 = time.perf_counter()
-        oracle.branch_norm_mean(ya.reshape(B, len(qrows), -1)[:, :nr], ys[:, :nr],
-                                prm["beta_a"], prm["beta_s"], shape.eps)
-        t_norm = time.perf_counter() - t0
-        est = t_rope + n_blocks * max(t_blk, 0.0) + (T / S) * t_ssm + (T / nr) * t_norm
+        est = _oracle_layer_estimate(shape, window, q, k, v, part, prm)
         per_role["global" if window <= 0 else "window"].append(est)
-        del q, k, v, part, ya, xc, ys
+        del q, k, v, part
     wall = time.perf_counter() - t_all0
     n_g = sum(1 for w, _ in roles if w <= 0)
     n_w = len(roles) - n_g
     t_stack = (n_g * sum(per_role["global"]) / len(per_role["global"])
                + n_w * sum(per_role["window"]) / len(per_role["window"]))
-    return {"value": shape.B * shape.T * len(roles) / t_stack, "unit": "tokens/s",
-            "cores": blas_threads() or 1, "host_cpus": len(os.sched_getaffinity(0)),
-            "cpu_model": cpu_model(), "kind": "oracle",
-            "seconds_per_stack_estimated": t_stack,
-            "sample": (f"stack32-b2-t16512 layers {list(CPU_STACK_LAYERS)}: per layer the "
-                       f"oracle attention over one {CPU_QUERY_BLOCK}-row query block plus its "
-                       f"K rotation, and conv + scan + norm over the first {CPU_SCAN_ROWS} "
-                       f"rows; extrapolated to {n_blocks} blocks and {T} rows per layer, then "
-                       f"to {n_g} global + {n_w} window layers; {wall:.1f} s of CPU work; "
-                       "tokens/s per layer as the GPU value")}
+    return _baseline_record(
+        shape.B * shape.T * len(roles) / t_stack, "tokens/s",
+        (f"stack32-b2-t16512 layers {list(CPU_STACK_LAYERS)}: per layer the "
+         f"oracle attention over one {CPU_QUERY_BLOCK}-row query block plus its "
+         f"K rotation, and conv + scan + norm over the first {CPU_SCAN_ROWS} "
+         f"rows; extrapolated to {n_blocks} blocks and {T} rows per layer, then "
+         f"to {n_g} global + {n_w} window layers; {wall:.1f} s of CPU work; "
+         "tokens/s per layer as the GPU value"),
+        seconds_per_stack_estimated=t_stack)
 
 
 def cpu_baseline_decode(shape, runs: int = 3):
@@ -733,6 +781,9 @@ def main():
                      "highest_level": sclk[0][1] if sclk else None,
                      "note": "the driver's current-clock line, read 12 times 1 ms apart while "
                              "layer calls run: an average including idle time"}}
+    if not args.no_cpu_baseline:
+        log("cpu baseline (swa-prefill layer)")
+        result["swa_prefill"]["cpu_baseline"] = cpu_baseline_layer(sshape, inp)
 
     # the same layer with the meta tokens cached (real-token rows only)
     from workloads import cached_meta_inputs
@@ -803,7 +854,8 @@ def main():
     # ------------------------------------------------------------ global-prefill layer
     log("global-prefill layer")
     gshape = GLOBAL_PREFILL
-    gt = to_device(prefill_inputs(gshape, 0), gshape.dtype)
+    ginp = prefill_inputs(gshape, 0)
+    gt = to_device(ginp, gshape.dtype)
     gsteps = max(5, args.steps // 2)
     gplan, gms = run_prefill(gshape, hm, gt, gsteps, 2, two_streams=False)
     gev = layer_events(gplan, gsteps, 1)
@@ -817,7 +869,10 @@ def main():
                                   "the layer's middle launch (attention | final scan)"),
         "attention_alone": mfma_roofline(gfl, gms_attn * 1e3, "attn_fwd_bf16",
                                          "attention alone over the prepared K/V")}
-    del gt, gplan
+    if not args.no_cpu_baseline:
+        log("cpu baseline (global-prefill sample)")
+        result["global_prefill"]["cpu_baseline"] = cpu_baseline_layer_sampled(gshape, ginp)
+    del gt, gplan, ginp
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ decode
