@@ -11,10 +11,10 @@
 // range [0, M + min(n_prev+1, W)).
 //
 // bf16 path: step_fused_bf16, one workgroup per (sequence, kv group, key split)
-// that streams its K/V tiles through LDS and also runs a share of the SSM step,
-// then step_combine (one workgroup per sequence) merges the key splits into
-// Y_attn and applies the branch RMS norm, rescale and average: two launches
-// per layer.
+// that streams its K/V tiles through LDS, plus workgroups that run the SSM
+// step, then step_combine (one workgroup per sequence) merges the key splits
+// into Y_attn and applies the branch RMS norm, rescale and average: two
+// launches per layer.
 // float32 path (Dh in {16, 32, 64}): SSM step + KV write, one thread per
 // (b, head) over all visible rows, then the same combine kernel.
 #include <algorithm>
@@ -205,9 +205,9 @@ constexpr int kDecStages = 3;   // 64-row K/V tiles in flight per workgroup (48 
 // online softmax per head, and O^T += V^T P^T with v_mfma_f32_16x16x16_bf16
 // (V^T read from the row-major tile).  The 4 waves merge in LDS and write one
 // partial (max, sum, unnormalised O) per head; step_combine merges the splits.
-// While its first tiles load, the workgroup also runs its share of the SSM
-// step (conv step + one scan step per (b, channel), in place on the states).
-// The workgroup whose rows hold the new token's slot (producer layer) first
+// The workgroups past the attention ones run the SSM step, one (b, channel)
+// item per thread (conv step + one scan step, in place on the states).  The
+// workgroup whose rows hold the new token's slot (producer layer) first
 // rotates k_new and writes k_new / v_new there.
 __global__ __launch_bounds__(256) void step_fused_bf16(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_new,
@@ -218,12 +218,12 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
     float* __restrict__ conv_state, float* __restrict__ ssm_state, float* __restrict__ ys_ws,
     size_t ys_stride, float* __restrict__ part, size_t part_b_stride, int Hq, int Hkv, int Di,
     int S, SeqPos sp, float qscale, double log2_base, double rstep,
-    int n_split, int tiles_per_split, int ssm_per_block, int n_ssm, int n_attn) {
+    int n_split, int tiles_per_split, int n_ssm, int n_attn) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kDecStages][2][8192];
   __shared__ float sm[4][16], sl[4][16];
   const int tid = threadIdx.x;
   if ((int)blockIdx.x >= n_attn) {
-    // workgroups past the attention ones run SSM-step items only
+    // workgroups past the attention ones: SSM-step items
     const int nb = (int)gridDim.x - n_attn;
     for (int j = ((int)blockIdx.x - n_attn) * 256 + tid; j < n_ssm; j += nb * 256) {
       const int bs = j / Di, c = j % Di;
@@ -262,41 +262,7 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
     __syncthreads();
   }
 
-  // 2) this workgroup's share of the SSM step, loads first: the first item of
-  // each thread is loaded now and computed after the attention loop, so the
-  // loads overlap the K/V stream (items past the first 256 run at the end)
-  const int sidx0 = blockIdx.x * ssm_per_block + tid;
-  const bool has_ssm = tid < ssm_per_block && sidx0 < n_ssm;
-  float4 sh[4], sa4[4], scw;
-  uint4 sbr[2], scr[2];
-  float ss0 = 0.f, ss1 = 0.f, ss2 = 0.f, sxv = 0.f, sdv = 0.f, szv = 0.f, sD = 0.f, scb = 0.f;
-  int sbq = 0, scq = 0;
-  if (has_ssm) {
-    sbq = sidx0 / Di;
-    scq = sidx0 % Di;
-    const size_t idx = (size_t)sbq * Di + scq;
-    const float* cs = conv_state + idx * 3;
-    ss0 = cs[0];
-    ss1 = cs[1];
-    ss2 = cs[2];
-    sxv = bf2f(x[idx]);
-    sdv = bf2f(dl[idx]);
-    szv = bf2f(z[idx]);
-    sD = D[scq];
-    scb = cb[scq];
-    scw = *(const float4*)(cw + (size_t)scq * 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sh[i] = ((const float4*)(ssm_state + idx * kNS))[i];
-      sa4[i] = ((const float4*)(A + (size_t)scq * kNS))[i];
-    }
-    sbr[0] = *(const uint4*)(Bm + (size_t)sbq * kNS);
-    sbr[1] = *(const uint4*)(Bm + (size_t)sbq * kNS + 8);
-    scr[0] = *(const uint4*)(Cm + (size_t)sbq * kNS);
-    scr[1] = *(const uint4*)(Cm + (size_t)sbq * kNS + 8);
-  }
-
-  // 3) the first two tiles: thread -> LDS rows 16 wave + 8 i + lane / 8, slot
+  // 2) the first two tiles: thread -> LDS rows 16 wave + 8 i + lane / 8, slot
   // lane & 7 (global_load_lds writes lane L of a wave at base + 16 L)
   const bf16_t* kb0 = kc + (size_t)b * S * rs + (size_t)g * 64;
   const bf16_t* vb0 = vc + (size_t)b * S * rs + (size_t)g * 64;
@@ -321,7 +287,7 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
   if (ntile > 0) issue(0);
   if (ntile > 1) issue(1);
 
-  // 4) Q^T fragment (B operand): lane holds head n of the group, dims 8G+e and 32+8G+e
+  // 3) Q^T fragment (B operand): lane holds head n of the group, dims 8G+e and 32+8G+e
   bf16x8_v qf[2];
   {
     const bf16_t* src = q + ((size_t)b * Hq + g * grp + min(n, grp - 1)) * 64;
@@ -346,7 +312,7 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
     }
   }
 
-  // 5) stream the tiles; per lane: head n, keys 16 wave + 4G + i of each tile
+  // 4) stream the tiles; per lane: head n, keys 16 wave + 4G + i of each tile
   const float NEG_INF = -__builtin_huge_valf();
   float m_run = -1e30f, l_run = 0.f;
   f32x4_v acc[4];
@@ -423,51 +389,7 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
 
-  // 6) the SSM step of this workgroup's items (conv step, scan step, gate)
-  if (has_ssm) {
-    const size_t idx = (size_t)sbq * Di + scq;
-    const float u = scb + scw.x * ss0 + scw.y * ss1 + scw.z * ss2 + scw.w * sxv;
-    float* cs = conv_state + idx * 3;
-    cs[0] = ss1;
-    cs[1] = ss2;
-    cs[2] = sxv;
-    const float xc = siluf_(u);
-    const float du = sdv * xc;
-    const float hv[kNS] = {sh[0].x, sh[0].y, sh[0].z, sh[0].w, sh[1].x, sh[1].y, sh[1].z, sh[1].w,
-                           sh[2].x, sh[2].y, sh[2].z, sh[2].w, sh[3].x, sh[3].y, sh[3].z, sh[3].w};
-    const float av[kNS] = {sa4[0].x, sa4[0].y, sa4[0].z, sa4[0].w, sa4[1].x, sa4[1].y,
-                           sa4[1].z, sa4[1].w, sa4[2].x, sa4[2].y, sa4[2].z, sa4[2].w,
-                           sa4[3].x, sa4[3].y, sa4[3].z, sa4[3].w};
-    const uint32_t bw[8] = {sbr[0].x, sbr[0].y, sbr[0].z, sbr[0].w,
-                            sbr[1].x, sbr[1].y, sbr[1].z, sbr[1].w};
-    const uint32_t cwd[8] = {scr[0].x, scr[0].y, scr[0].z, scr[0].w,
-                             scr[1].x, scr[1].y, scr[1].z, scr[1].w};
-    float hn[kNS];
-    float y4[4] = {sD * xc, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int nn = 0; nn < kNS; ++nn) {
-      const uint32_t wb = bw[nn >> 1], wc = cwd[nn >> 1];
-      const float bv = __uint_as_float((nn & 1) ? (wb & 0xffff0000u) : (wb << 16));
-      const float cv = __uint_as_float((nn & 1) ? (wc & 0xffff0000u) : (wc << 16));
-      hn[nn] = fast_exp2(sdv * (av[nn] * kLog2e)) * hv[nn] + du * bv;
-      y4[nn & 3] += cv * hn[nn];
-    }
-    float4* hs = (float4*)(ssm_state + idx * kNS);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      hs[i] = make_float4(hn[4 * i], hn[4 * i + 1], hn[4 * i + 2], hn[4 * i + 3]);
-    ys_ws[(size_t)sbq * ys_stride + scq] = ((y4[0] + y4[1]) + (y4[2] + y4[3])) * siluf_(szv);
-  }
-  for (int j = tid + 256; j < ssm_per_block; j += 256) {
-    const int sidx = blockIdx.x * ssm_per_block + j;
-    if (sidx < n_ssm) {
-      const int bs = sidx / Di, c = sidx % Di;
-      ys_ws[(size_t)bs * ys_stride + c] =
-          ssm_step_one<bf16_t>(bs, c, Di, x, dl, Bm, Cm, z, A, D, cw, cb, conv_state, ssm_state);
-    }
-  }
-
-  // 7) merge the 4 waves: (max, sum) per head and O^T (dims 16 db + 4G + i, head n)
+  // 5) merge the 4 waves: (max, sum) per head and O^T (dims 16 db + 4G + i, head n)
   __syncthreads();                                  // every wave is done with the ring
   float* sO = (float*)&ring[0][0][0];               // [wave][head 16][dim 64]
   if (G == 0) {
@@ -613,11 +535,9 @@ struct StepGeom {
 // bf16 decode: key splits of whole 64-row tiles, about kDecBlocks workgroups
 // in all (two to three per CU stream at once with 48 KB of LDS each).
 constexpr int kDecBlocks = 640;
-// SSM-step items per thread of the workgroups that run only the SSM step
-// (measured: 1 item per thread in workgroups of their own beats a share of
-// every attention workgroup, which kept the stream's tail waiting on the
-// exponentials; 0 selects that shared form)
-constexpr int kSsmItems = 1;
+// The SSM step runs in workgroups of its own, one item per thread (measured:
+// faster than a share of every attention workgroup, which kept the stream's
+// tail waiting on the exponentials, and than 4 items per thread).
 
 StepGeom step_geom(const hm_step_args* a) {
   StepGeom s{};
@@ -771,10 +691,7 @@ hm_status mixer_step_impl(const hm_step_args* a, void* ws, size_t ws_bytes, void
   if (a->dtype == HM_BF16) {
     const int n_attn = a->B * a->Hkv * g.n_split;
     const int n_ssm = a->B * a->Di;
-    // SSM-step items: a share of every attention workgroup, or (kSsmItems > 0)
-    // workgroups of their own with kSsmItems items per thread
-    const int ssm_per_block = kSsmItems > 0 ? 0 : (n_ssm + n_attn - 1) / n_attn;
-    const int n_ssm_blocks = kSsmItems > 0 ? (n_ssm + 256 * kSsmItems - 1) / (256 * kSsmItems) : 0;
+    const int n_ssm_blocks = (n_ssm + 255) / 256;   // one SSM-step item per thread
     hipLaunchKernelGGL(step_fused_bf16, dim3(n_attn + n_ssm_blocks), dim3(256), 0, st,
                        (const bf16_t*)a->q, (const bf16_t*)a->k_new, (const bf16_t*)a->v_new,
                        (bf16_t*)a->k_cache, (bf16_t*)a->v_cache, (const bf16_t*)a->x,
@@ -782,7 +699,7 @@ hm_status mixer_step_impl(const hm_step_args* a, void* ws, size_t ws_bytes, void
                        (const bf16_t*)a->z, a->A, a->D, a->conv_w, a->conv_b, a->conv_state,
                        a->ssm_state, ys_ws, g.ys_stride, part, g.part_b_stride, a->Hq, a->Hkv,
                        a->Di, S, sp, sc, l2b, exp2(-l2b / 32.0), g.n_split,
-                       g.tiles_per_split, ssm_per_block, n_ssm, n_attn);
+                       g.tiles_per_split, n_ssm, n_attn);
     hm_status s = hm::check_launch("step_fused_bf16");
     if (s != HM_OK) return s;
     hipLaunchKernelGGL(step_combine<bf16_t>, dim3(a->B), dim3(kCombThreads), 0, st,
