@@ -55,7 +55,8 @@ struct Vec8<float> {  // 8 floats = two 16-byte accesses
   }
 };
 
-// Rows of up to 64 * 8 * kMaxC elements are held in registers (norm_mean_rows).
+// Rows of up to 64 * 8 * kMaxC elements are held in registers (norm_mean_rows,
+// norm_mean_rows_bf16, rms_norm_rows).
 constexpr int kMaxC = 4;
 
 // width % 8 == 0 (16-byte aligned rows), wider than 64 * 8 * kMaxC: one wave
