@@ -208,7 +208,11 @@ def test_conv_selective_scan(shape, use_state):
 @pytest.mark.parametrize("dtype,width,rows", [("f32", 32, 64), ("bf16", 1600, 2176),
                                               ("bf16", 1600, 3), ("f32", 37, 5),
                                               ("bf16", 200, 9), ("bf16", 2400, 7),
-                                              ("f32", 2048, 6)])
+                                              ("f32", 2048, 6),
+                                              # packed bf16 rows: the widest (2048), one
+                                              # 8-element chunk, and 65 chunks (lane 0 two)
+                                              ("bf16", 2048, 5), ("bf16", 8, 4),
+                                              ("bf16", 520, 33)])
 def test_branch_norm_mean(dtype, width, rows):
     rng = np.random.default_rng(width)
     from workloads import bf16_round
