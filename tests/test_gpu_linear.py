@@ -27,7 +27,10 @@ def setup_module(module):
                                       # 256 x 256 tiles (ragged in both directions)
                                       (4100, 320, [1600, 16, 2384]), (8192, 64, [4096]),
                                       # 192 tiles (the 256 x 256 kernel) and 189 (128 x 128)
-                                      (3000, 128, [16, 4080]), (2304, 64, [5376])])
+                                      (3000, 128, [16, 4080]), (2304, 64, [5376]),
+                                      # one tile column, 201 tile rows (last group of the
+                                      # grouped tile order holds one row)
+                                      (51300, 64, [200])])
 def test_linear_bf16(M, K, segs):
     rng = np.random.default_rng(M + K)
     x = bf16_round(rng.standard_normal((M, K)))
