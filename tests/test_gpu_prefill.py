@@ -91,6 +91,35 @@ def test_attention_bf16(B, M, N, Hq, Hkv, W):
     assert_close(got, ref, "bf16", "attention bf16")
 
 
+# positions offset by pos0 (a continued sequence; the angles reach 1e5 rad, where
+# the kernels' double-precision reduction to revolutions matters) and a caller's
+# softmax scale, through the standalone attention and the fused layer
+@pytest.mark.parametrize("dtype,pos0,scale", [("f32", 37, 0.3), ("bf16", 5, 0.0),
+                                              ("bf16", 100_000, 0.1)])
+def test_attention_pos0_and_scale(dtype, pos0, scale):
+    shape = with_(SWA_PREFILL, N=260, M=12, W=96, Hq=4, Hkv=2, Di=256, dtype=dtype)
+    if dtype == "f32":
+        shape = with_(shape, Hq=2, Hkv=1, Di=128, Dh=64)
+    inp = prefill_inputs(shape, 7)
+    t = up_inputs(inp, dtype)
+    o = hm.swa_meta_attn(t["q"], t["k"], t["v"], shape.M, shape.W, shape.rope_base,
+                         pos0=pos0, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention(inp["q"], inp["k"], inp["v"], shape.M, shape.W, shape.rope_base,
+                           pos0=pos0, scale=scale)
+    assert_close(down(o), ref, dtype, "attention with pos0 / scale")
+
+
+def test_mixer_prefill_bf16_pos0_and_scale():
+    shape = with_(SWA_PREFILL, N=400, M=16, W=128)
+    inp = prefill_inputs(shape, 8)
+    r = hm.mixer_prefill(up_inputs(inp, "bf16"), shape.M, shape.W, pos0=4321, scale=0.11)
+    torch.cuda.synchronize()
+    ref = oracle.mixer_prefill(inp, shape.M, shape.W, pos0=4321, scale=0.11)
+    for k in ("ya", "ys", "out"):
+        assert_close(down(r[k]), ref[k], "bf16", f"mixer {k} with pos0 / scale")
+
+
 def test_attention_bf16_global_full_size_sampled_rows():
     # the global-attention workload at full size (B=4, T=8320), rows sampled
     # across tile boundaries, the meta prefix and the end
