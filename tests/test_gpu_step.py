@@ -22,26 +22,26 @@ def setup_module(module):
         pytest.skip("no GPU")
 
 
-def _run_pair(shape, seed):
+def _run_pair(shape, seed, scale=0.0):
     d = decode_inputs(shape, seed)
     t = up_inputs(d, shape.dtype)
     kc, vc = t["k_cache"], t["v_cache"]
     pa = hm.StepPlan(t["a"], kc, vc, shape.n_prev, shape.M, shape.W, rope_base=shape.rope_base,
-                     eps=shape.eps, want_branches=True)
+                     eps=shape.eps, scale=scale, want_branches=True)
     pb = hm.StepPlan(t["b"], kc, vc, shape.n_prev, shape.M, shape.W, rope_base=shape.rope_base,
-                     eps=shape.eps, want_branches=True)
+                     eps=shape.eps, scale=scale, want_branches=True)
     pa.run()
     pb.run()
     torch.cuda.synchronize()
     ra = oracle.mixer_step(d["a"], d["k_cache"], d["v_cache"], shape.n_prev, shape.M, shape.W,
-                           producer=True, rope_base=shape.rope_base, eps=shape.eps)
+                           producer=True, rope_base=shape.rope_base, eps=shape.eps, scale=scale)
     rb = oracle.mixer_step(d["b"], ra["k_cache"], ra["v_cache"], shape.n_prev, shape.M, shape.W,
-                           producer=False, rope_base=shape.rope_base, eps=shape.eps)
+                           producer=False, rope_base=shape.rope_base, eps=shape.eps, scale=scale)
     return d, t, (pa, pb), (ra, rb)
 
 
-def _check(shape, seed):
-    d, t, plans, refs = _run_pair(shape, seed)
+def _check(shape, seed, scale=0.0):
+    d, t, plans, refs = _run_pair(shape, seed, scale)
     dt = shape.dtype
     for name, plan, ref in zip("ab", plans, refs):
         assert_close(down(plan.out), ref["out"], dt, f"{name} out")
@@ -59,6 +59,15 @@ def _check(shape, seed):
     others = [r for r in range(kc.shape[1]) if r != slot]
     assert np.array_equal(kc[:, others], d["k_cache"][:, others].astype(np.float64))
 
+
+
+# a caller's softmax scale and another RoPE base (the cache built with that base)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_step_scale_and_rope_base(dtype):
+    shape = with_(DECODE_PAIR, B=3, n_prev=1700, rope_base=500000.0, dtype=dtype)
+    if dtype == "f32":
+        shape = with_(shape, Hq=4, Hkv=2, Dh=32, Di=128)
+    _check(shape, 9, scale=0.2)
 
 def test_decode_pair_full_size():
     _check(DECODE_PAIR, 0)
