@@ -81,6 +81,8 @@ BF16_CASES = [
     (1, 3, 200, 4, 1, 1),
     (1, 128, 2048, 25, 5, 1024),
     (1, 70, 450, 6, 3, 64),
+    # every row a meta row (causal among themselves, the window never applies)
+    (2, 150, 0, 2, 1, 16),
 ]
 
 
