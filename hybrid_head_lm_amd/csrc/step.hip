@@ -345,9 +345,14 @@ __global__ __launch_bounds__(256) void step_fused_bf16(
     for (int u = 0; u < kDecStages; ++u) {
       const int t = t0 + u;
       if (t >= ntile) break;
+      // A wave reads only the 16 rows of each tile it loaded itself (K rows
+      // 16 wave.., V^T keys 16 wave..), so waiting for its own loads suffices:
+      // no workgroup barrier per tile (measured: cold pair 57.1 -> 56.5 us).
+      // Slot (t+2) % 3 held tile t-1, whose reads this wave finished last step.
       if (t == 0 || t + 1 >= ntile) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));   // tile t+1 may stay in flight
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
       if (t + 2 < ntile) issue(t + 2);
       const unsigned char* sk = ring[u][0];
       const unsigned char* sv = ring[u][1];
