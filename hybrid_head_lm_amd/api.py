@@ -1,9 +1,12 @@
 """torch-facing wrappers of the libhm C ABI (argument marshalling only).
 
-Every function takes contiguous CUDA (HIP) tensors, passes their device
-pointers and the current stream to the library, and raises HmError with the
-library's message on any non-zero status.  Workspaces are allocated here with
-torch (the library itself never allocates).
+Every function takes contiguous CUDA (HIP) tensors on one device, passes
+their device pointers and the current stream to the library, and raises
+HmError with the library's message on any non-zero status.  The library sees
+plain pointers and cannot know a buffer's size, so every tensor is checked
+here against the element count and dtype the call implies (ValueError before
+any launch; a view of another shape over the same elements is accepted).  Workspaces are allocated here with torch (the library
+itself never allocates).
 """
 from __future__ import annotations
 
@@ -52,8 +55,32 @@ def _dev(*ts):
             raise ValueError("libhm takes device tensors")
         if not t.is_contiguous():
             raise ValueError("libhm takes contiguous tensors")
+        if dev is not None and t.device != dev:
+            raise ValueError("libhm takes tensors on one device")
         dev = t.device
     return dev
+
+
+def _expect(name, t, shape, dtype=None):
+    """Raise unless t (when given) holds as many elements as `shape` (any view
+    of the same contiguous buffer will do) and has this dtype."""
+    if t is None:
+        return
+    n = 1
+    for d in shape:
+        n *= int(d)
+    if t.numel() != n or (dtype is not None and t.dtype != dtype):
+        want = str(tuple(shape)) + ("" if dtype is None else f" {dtype}")
+        raise ValueError(f"{name}: expected {want}, got {tuple(t.shape)} {t.dtype}")
+
+
+def _rank(name, t, n):
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions, got {tuple(t.shape)}")
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
 
 
 def _f32(*ts):
@@ -70,18 +97,21 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 def swa_meta_attn(q, k, v, n_meta: int, window: int, rope_base: float = 10000.0,
                   pos0: int = 0, scale: float = 0.0, out=None, workspace=None):
     """O = attention over X~ (meta prefix + causal sliding window), GQA, RoPE."""
-    dev = _dev(q, k, v, out)
+    dev = _dev(q, k, v, out, workspace)
+    _rank("q", q, 4)
+    _rank("k", k, 4)
     B, T, Hq, Dh = q.shape
     Hkv = k.shape[2]
-    if k.shape != (B, T, Hkv, Dh) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("k, v must be [B, T, Hkv, Dh] with q's dtype")
+    _expect("k", k, (B, T, Hkv, Dh), q.dtype)
+    _expect("v", v, (B, T, Hkv, Dh), q.dtype)
+    _expect("out", out, q.shape, q.dtype)
     dt = dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
     nb = lib.hm_swa_meta_attn_workspace(B, T, Hkv, Dh, dt)
     ws = workspace if workspace is not None else _ws(nb, dev)
     _check(lib.hm_swa_meta_attn(_p(q), _p(k), _p(v), _p(out), B, T, Hq, Hkv, Dh, n_meta, window,
-                                rope_base, pos0, scale, dt, _p(ws), ws.numel(), _stream()))
+                                rope_base, pos0, scale, dt, _p(ws), _nbytes(ws), _stream()))
     return out
 
 
@@ -93,12 +123,14 @@ def attn_kv_bytes(B: int, T: int, Hkv: int, Dh: int, dtype) -> int:
 def attn_kv_prepare(k, v, rope_base: float = 10000.0, pos0: int = 0, kv=None):
     """Rotate k and lay out k, v for the attention kernel; returns the kv buffer."""
     dev = _dev(k, v, kv)
+    _rank("k", k, 4)
+    _expect("v", v, k.shape, k.dtype)
     B, T, Hkv, Dh = k.shape
     dt = dtype_code(k)
     nb = lib.hm_attn_kv_bytes(B, T, Hkv, Dh, dt)
     if kv is None:
         kv = _ws(nb, dev)
-    _check(lib.hm_attn_kv_prepare(_p(k), _p(v), _p(kv), kv.numel() * kv.element_size(), B, T,
+    _check(lib.hm_attn_kv_prepare(_p(k), _p(v), _p(kv), _nbytes(kv), B, T,
                                   Hkv, Dh, rope_base, pos0, dt, _stream()))
     return kv
 
@@ -107,10 +139,12 @@ def attn_with_kv(q, kv, Hkv: int, n_meta: int, window: int, rope_base: float = 1
                  pos0: int = 0, scale: float = 0.0, out=None):
     """Attention of q over a buffer filled by attn_kv_prepare (same rope_base, pos0)."""
     _dev(q, kv, out)
+    _rank("q", q, 4)
     B, T, Hq, Dh = q.shape
+    _expect("out", out, q.shape, q.dtype)
     if out is None:
         out = torch.empty_like(q)
-    _check(lib.hm_attn_with_kv(_p(q), _p(kv), kv.numel() * kv.element_size(), _p(out), B, T, Hq,
+    _check(lib.hm_attn_with_kv(_p(q), _p(kv), _nbytes(kv), _p(out), B, T, Hq,
                                Hkv, Dh, n_meta, window, rope_base, pos0, scale, dtype_code(q),
                                _stream()))
     return out
@@ -120,8 +154,15 @@ def attn_with_kv(q, kv, Hkv: int, n_meta: int, window: int, rope_base: float = 1
 def causal_conv1d(x, w, bias=None, state_in=None, apply_silu=True, state_out=None, out=None):
     dev = _dev(x, w, bias, state_in, state_out, out)
     _f32(w, bias, state_in, state_out)
+    _rank("x", x, 3)
+    _rank("w", w, 2)
     B, T, Di = x.shape
     K = w.shape[1]
+    _expect("w", w, (Di, K))
+    _expect("bias", bias, (Di,))
+    _expect("state_in", state_in, (B, Di, K - 1))
+    _expect("state_out", state_out, (B, Di, K - 1))
+    _expect("out", out, x.shape, x.dtype)
     if out is None:
         out = torch.empty_like(x)
     _check(lib.hm_causal_conv1d(_p(x), _p(w), _p(bias), _p(state_in), _p(out), _p(state_out), B, T,
@@ -129,29 +170,53 @@ def causal_conv1d(x, w, bias=None, state_in=None, apply_silu=True, state_out=Non
     return out
 
 
-def selective_scan(x, delta, A, Bm, Cm, D=None, z=None, h0=None, h_out=None, out=None,
-                   workspace=None):
-    dev = _dev(x, delta, A, Bm, Cm, D, z, h0, h_out, out)
-    _f32(A, D, h0, h_out)
+def _scan_shapes(x, delta, A, Bm, Cm, D, z, h0, h_out, out):
     B, T, Di = x.shape
     N = A.shape[1]
+    _expect("A", A, (Di, N))
+    for name, t in (("delta", delta), ("z", z), ("out", out)):
+        _expect(name, t, x.shape, x.dtype)
+    _expect("Bm", Bm, (B, T, N), x.dtype)
+    _expect("Cm", Cm, (B, T, N), x.dtype)
+    _expect("D", D, (Di,))
+    _expect("h0", h0, (B, Di, N))
+    _expect("h_out", h_out, (B, Di, N))
+
+
+def selective_scan(x, delta, A, Bm, Cm, D=None, z=None, h0=None, h_out=None, out=None,
+                   workspace=None):
+    dev = _dev(x, delta, A, Bm, Cm, D, z, h0, h_out, out, workspace)
+    _f32(A, D, h0, h_out)
+    _rank("x", x, 3)
+    _rank("A", A, 2)
+    B, T, Di = x.shape
+    N = A.shape[1]
+    _scan_shapes(x, delta, A, Bm, Cm, D, z, h0, h_out, out)
     if out is None:
         out = torch.empty_like(x)
     nb = lib.hm_selective_scan_workspace(B, T, Di, N)
     ws = workspace if workspace is not None else _ws(nb, dev)
     _check(lib.hm_selective_scan(_p(x), _p(delta), _p(A), _p(Bm), _p(Cm), _p(D), _p(z), _p(h0),
                                  _p(out), _p(h_out), B, T, Di, N, dtype_code(x), _p(ws),
-                                 ws.numel(), _stream()))
+                                 _nbytes(ws), _stream()))
     return out
 
 
 def conv_selective_scan(x, conv_w, conv_b, delta, A, Bm, Cm, D=None, z=None, conv_state_in=None,
                         conv_state_out=None, h0=None, h_out=None, out=None, workspace=None):
     dev = _dev(x, conv_w, conv_b, delta, A, Bm, Cm, D, z, conv_state_in, conv_state_out, h0,
-               h_out, out)
+               h_out, out, workspace)
     _f32(conv_w, conv_b, A, D, conv_state_in, conv_state_out, h0, h_out)
+    _rank("x", x, 3)
+    _rank("A", A, 2)
+    _rank("conv_w", conv_w, 2)
     B, T, Di = x.shape
     N, K = A.shape[1], conv_w.shape[1]
+    _scan_shapes(x, delta, A, Bm, Cm, D, z, h0, h_out, out)
+    _expect("conv_w", conv_w, (Di, K))
+    _expect("conv_b", conv_b, (Di,))
+    _expect("conv_state_in", conv_state_in, (B, Di, K - 1))
+    _expect("conv_state_out", conv_state_out, (B, Di, K - 1))
     if out is None:
         out = torch.empty_like(x)
     nb = lib.hm_selective_scan_workspace(B, T, Di, N)
@@ -159,7 +224,7 @@ def conv_selective_scan(x, conv_w, conv_b, delta, A, Bm, Cm, D=None, z=None, con
     _check(lib.hm_conv_selective_scan(_p(x), _p(conv_w), _p(conv_b), _p(conv_state_in),
                                       _p(conv_state_out), _p(delta), _p(A), _p(Bm), _p(Cm), _p(D),
                                       _p(z), _p(h0), _p(out), _p(h_out), B, T, Di, K, N,
-                                      dtype_code(x), _p(ws), ws.numel(), _stream()))
+                                      dtype_code(x), _p(ws), _nbytes(ws), _stream()))
     return out
 
 
@@ -169,6 +234,10 @@ def branch_norm_mean(ya, ys, beta_a, beta_s, eps: float = 1e-6, out=None):
     _f32(beta_a, beta_s)
     width = ya.shape[-1]
     rows = ya.numel() // width
+    _expect("ys", ys, ya.shape, ya.dtype)
+    _expect("beta_a", beta_a, (width,))
+    _expect("beta_s", beta_s, (width,))
+    _expect("out", out, ya.shape, ya.dtype)
     if out is None:
         out = torch.empty_like(ya)
     _check(lib.hm_branch_norm_mean(_p(ya), _p(ys), _p(beta_a), _p(beta_s), eps, _p(out), rows,
@@ -190,13 +259,21 @@ def linear(x, w, seg_cols=None, outs=None, epilogues=None):
     _dev(x, w)
     if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
         raise TypeError("linear takes bf16 x and w")
+    _rank("w", w, 2)
     K = x.shape[-1]
     M = x.numel() // K
     N = w.shape[0]
+    _expect("w", w, (N, K))
     cols = [N] if seg_cols is None else list(seg_cols)
+    if sum(cols) != N:
+        raise ValueError(f"seg_cols must add up to the {N} rows of w")
     if outs is None:
         outs = [torch.empty(x.shape[:-1] + (c,), dtype=x.dtype, device=x.device) for c in cols]
-    _dev(*outs)
+    if len(outs) != len(cols):
+        raise ValueError("one output tensor per segment")
+    _dev(x, *outs)
+    for i, (o, c) in enumerate(zip(outs, cols)):
+        _expect(f"outs[{i}]", o, x.shape[:-1] + (c,), torch.bfloat16)
     ptrs = (ctypes.c_void_p * len(cols))(*[o.data_ptr() for o in outs])
     widths = (ctypes.c_int * len(cols))(*cols)
     if epilogues is None:
@@ -205,11 +282,13 @@ def linear(x, w, seg_cols=None, outs=None, epilogues=None):
         if len(epilogues) != len(cols):
             raise ValueError("one epilogue per segment")
         eps = (LinearEpilogue * len(cols))()
-        for e, d in zip(eps, epilogues):
+        for i, (e, d, c) in enumerate(zip(eps, epilogues, cols)):
             d = d or {}
             bias, res = d.get("bias"), d.get("residual")
-            _dev(bias, res)
+            _dev(x, bias, res)
             _f32(bias)
+            _expect(f"epilogues[{i}].bias", bias, (c,))
+            _expect(f"epilogues[{i}].residual", res, x.shape[:-1] + (c,), torch.bfloat16)
             if d.get("act") not in _ACTS:
                 raise ValueError(f"unknown activation {d.get('act')!r}")
             e.bias = None if bias is None else bias.data_ptr()
@@ -222,11 +301,12 @@ def linear(x, w, seg_cols=None, outs=None, epilogues=None):
 
 def rms_norm(x, w, eps: float = 1e-6, out=None):
     """x / sqrt(mean(x^2) + eps) * w over the last dim (w float32)."""
-    _dev(x, w)
+    _dev(x, w, out)
     _f32(w)
-    out = torch.empty_like(x) if out is None else out
-    _dev(out)
     width = x.shape[-1]
+    _expect("w", w, (width,))
+    _expect("out", out, x.shape, x.dtype)
+    out = torch.empty_like(x) if out is None else out
     _check(lib.hm_rms_norm(_p(x), _p(w), eps, _p(out), x.numel() // width, width, dtype_code(x),
                            _stream()))
     return out
@@ -250,12 +330,26 @@ class BlockPlan:
         dev = _dev(hidden, *[w[k] for k in keys])
         _f32(*[w[k] for k in ("ln1", "ln2", "dt_bias", "A", "D", "conv_w", "conv_b", "beta_a",
                               "beta_s")])
+        _rank("hidden", hidden, 3)
+        for k in ("A", "conv_w", "w_up"):
+            _rank(k, w[k], 2)
         B, T, d_model = hidden.shape
         Di, N = w["A"].shape
         Dh = Di // Hq
+        d_ffn, K = w["w_up"].shape[0], w["conv_w"].shape[1]
+        act = hidden.dtype
+        n_in = Hq * Dh + (0 if kv_reuse else 2 * Hkv * Dh) + 2 * Di
+        for k, shape, dt in (("ln1", (d_model,), None), ("ln2", (d_model,), None),
+                             ("w_in", (n_in, d_model), act), ("w_dbc", (Di + 2 * N, Di), act),
+                             ("dt_bias", (Di,), None), ("D", (Di,), None),
+                             ("conv_w", (Di, K), None), ("conv_b", (Di,), None),
+                             ("beta_a", (Di,), None), ("beta_s", (Di,), None),
+                             ("w_out", (d_model, Di), act), ("w_up", (d_ffn, d_model), act),
+                             ("w_down", (d_model, d_ffn), act)):
+            _expect(k, w[k], shape, dt)
         a = BlockArgs()
-        a.B, a.T, a.d_model, a.d_ffn = B, T, d_model, w["w_up"].shape[0]
-        a.Hq, a.Hkv, a.Dh, a.Di, a.N, a.K = Hq, Hkv, Dh, Di, N, w["conv_w"].shape[1]
+        a.B, a.T, a.d_model, a.d_ffn = B, T, d_model, d_ffn
+        a.Hq, a.Hkv, a.Dh, a.Di, a.N, a.K = Hq, Hkv, Dh, Di, N, K
         a.n_meta, a.window, a.pos0 = n_meta, window, pos0
         a.rope_base, a.scale, a.eps, a.dtype = rope_base, scale, eps, dtype_code(hidden)
         a.hidden = hidden.data_ptr()
@@ -266,10 +360,11 @@ class BlockPlan:
                 raise ValueError("kv_reuse needs the producer's kv buffer")
             kv = _ws(lib.hm_attn_kv_bytes(B, T, Hkv, Dh, dtype_code(hidden)), dev)
         self.kv = kv
-        a.kv, a.kv_bytes, a.kv_reuse = kv.data_ptr(), kv.numel() * kv.element_size(), int(kv_reuse)
+        a.kv, a.kv_bytes, a.kv_reuse = kv.data_ptr(), _nbytes(kv), int(kv_reuse)
         nb = lib.hm_block_prefill_workspace(ctypes.byref(a))
         self.ws = workspace if workspace is not None else _ws(nb, dev)
-        a.workspace, a.workspace_bytes = self.ws.data_ptr(), self.ws.numel()
+        _dev(hidden, kv, self.ws)
+        a.workspace, a.workspace_bytes = self.ws.data_ptr(), _nbytes(self.ws)
         self.args, self.w, self.hidden = a, w, hidden
 
     def run(self, stream=None):
@@ -303,8 +398,28 @@ class PrefillPlan:
         if not kv_reuse:
             _dev(t["k"], t["v"])
         _f32(t["A"], t["D"], t["conv_w"], t["conv_b"], t["beta_a"], t["beta_s"])
+        _rank("q", q, 4)
+        for k in ("x", "A", "conv_w"):
+            _rank(k, t[k], {"x": 3}.get(k, 2))
         B, T, Hq, Dh = q.shape
         Di = t["x"].shape[2]
+        N, K = t["A"].shape[1], t["conv_w"].shape[1]
+        Hkv = t["Hkv"] if "Hkv" in t else t["k"].shape[2]
+        _expect("x", t["x"], (B, T, Di), q.dtype)
+        _scan_shapes(t["x"], t["delta"], t["A"], t["Bm"], t["Cm"], t["D"], t["z"], h0, None, None)
+        if not kv_reuse:
+            _expect("k", t["k"], (B, T, Hkv, Dh), q.dtype)
+            _expect("v", t["v"], (B, T, Hkv, Dh), q.dtype)
+        for k in ("conv_b", "beta_a", "beta_s"):
+            _expect(k, t[k], (Di,))
+        _expect("conv_w", t["conv_w"], (Di, K))
+        for name, o in (("out", out), ("ya", ya), ("ys", ys)):
+            _expect(name, o, (B, T, Di), q.dtype)
+        if meta is not None:
+            _expect("meta k", meta["k"], (n_meta, Hkv, Dh), q.dtype)
+            _expect("meta v", meta["v"], (n_meta, Hkv, Dh), q.dtype)
+        _expect("conv_state_in", conv_state_in, (B, Di, K - 1))
+        _dev(q, out, ya, ys, kv, workspace)
         self.t = t
         self.ya = ya if ya is not None else torch.empty((B, T, Di), dtype=q.dtype, device=dev)
         self.ys = ys if ys is not None else torch.empty((B, T, Di), dtype=q.dtype, device=dev)
@@ -315,9 +430,8 @@ class PrefillPlan:
                                           device=dev)
             self.h = torch.empty((B, Di, t["A"].shape[1]), dtype=torch.float32, device=dev)
         a = PrefillArgs()
-        Hkv = t["Hkv"] if "Hkv" in t else t["k"].shape[2]
         a.B, a.T, a.Hq, a.Hkv, a.Dh, a.Di = B, T, Hq, Hkv, Dh, Di
-        a.N, a.K, a.n_meta, a.window = t["A"].shape[1], t["conv_w"].shape[1], n_meta, window
+        a.N, a.K, a.n_meta, a.window = N, K, n_meta, window
         a.pos0, a.rope_base, a.scale, a.eps, a.dtype = pos0, rope_base, scale, eps, dtype_code(q)
         for k in ("q", "x", "delta", "Bm", "Cm", "z", "A", "D", "conv_w", "conv_b",
                   "beta_a", "beta_s"):
@@ -339,7 +453,7 @@ class PrefillPlan:
         if kv is None:
             kv = _ws(lib.hm_attn_kv_bytes(B, key_rows, Hkv, Dh, dtype_code(q)), dev)
         self.kv = kv
-        a.kv, a.kv_bytes, a.kv_reuse = kv.data_ptr(), kv.numel() * kv.element_size(), int(kv_reuse)
+        a.kv, a.kv_bytes, a.kv_reuse = kv.data_ptr(), _nbytes(kv), int(kv_reuse)
         self.stream2 = stream2
         a.stream2 = stream2.cuda_stream if stream2 is not None else None
         a.ya, a.ys, a.out = self.ya.data_ptr(), self.ys.data_ptr(), self.out.data_ptr()
@@ -347,7 +461,7 @@ class PrefillPlan:
         a.h_out = self.h.data_ptr() if want_states else None
         nb = lib.hm_mixer_prefill_workspace(ctypes.byref(a))
         self.ws = workspace if workspace is not None else _ws(nb, dev)
-        a.workspace, a.workspace_bytes = self.ws.data_ptr(), self.ws.numel()
+        a.workspace, a.workspace_bytes = self.ws.data_ptr(), _nbytes(self.ws)
         self.args = a
 
     def run(self, stream=None, events=None):
@@ -396,12 +510,33 @@ class StepPlan:
                                         "A", "D", "conv_w", "conv_b", "beta_a", "beta_s")])
         _f32(layer["conv_state"], layer["ssm_state"], layer["A"], layer["D"], layer["conv_w"],
              layer["conv_b"], layer["beta_a"], layer["beta_s"])
+        _rank("q", q, 3)
+        _rank("k_cache", k_cache, 4)
+        for k in ("x", "A", "conv_w"):
+            _rank(k, layer[k], 2)
         B, Hq, Dh = q.shape
+        S, Hkv = k_cache.shape[1], k_cache.shape[2]
         Di = layer["x"].shape[1]
+        N, K = layer["A"].shape[1], layer["conv_w"].shape[1]
+        act = q.dtype
+        for k, shape, dt in (("k_cache", (B, S, Hkv, Dh), act), ("x", (B, Di), act),
+                             ("delta", (B, Di), act), ("z", (B, Di), act), ("Bm", (B, N), act),
+                             ("Cm", (B, N), act), ("A", (Di, N), None), ("D", (Di,), None),
+                             ("conv_w", (Di, K), None), ("conv_b", (Di,), None),
+                             ("conv_state", (B, Di, K - 1), None),
+                             ("ssm_state", (B, Di, N), None), ("beta_a", (Di,), None),
+                             ("beta_s", (Di,), None)):
+            _expect(k, k_cache if k == "k_cache" else layer[k], shape, dt)
+        _expect("v_cache", v_cache, k_cache.shape, act)
+        if producer:
+            _expect("k_new", layer["k_new"], (B, Hkv, Dh), act)
+            _expect("v_new", layer.get("v_new"), (B, Hkv, Dh), act)
+        _expect("out", out, (B, Di), act)
+        _dev(q, out, workspace)
         a = StepArgs()
-        a.B, a.Hq, a.Hkv, a.Dh, a.Di = B, Hq, k_cache.shape[2], Dh, Di
-        a.N, a.K, a.n_meta, a.window = layer["A"].shape[1], layer["conv_w"].shape[1], n_meta, window
-        a.cache_slots = k_cache.shape[1] - n_meta
+        a.B, a.Hq, a.Hkv, a.Dh, a.Di = B, Hq, Hkv, Dh, Di
+        a.N, a.K, a.n_meta, a.window = N, K, n_meta, window
+        a.cache_slots = S - n_meta
         a.n_prev, a.rope_base, a.scale, a.eps, a.dtype = n_prev, rope_base, scale, eps, dtype_code(q)
         a.q = q.data_ptr()
         a.k_new = layer["k_new"].data_ptr() if producer else None
@@ -424,7 +559,7 @@ class StepPlan:
             a.n_prev_seq = n_prev_seq.data_ptr()
         nb = lib.hm_mixer_step_workspace(ctypes.byref(a))
         self.ws = workspace if workspace is not None else _ws(nb, dev)
-        a.workspace, a.workspace_bytes = self.ws.data_ptr(), self.ws.numel()
+        a.workspace, a.workspace_bytes = self.ws.data_ptr(), _nbytes(self.ws)
         self.args = a
         self._keep = (layer, k_cache, v_cache, n_prev_seq)
 
