@@ -612,7 +612,7 @@ hm_status hm_debug_step_positions(int B, long long n_prev, const int* n_prev_seq
 
 namespace {
 
-hm_status step_scratch_ptr(void** out);
+hm_status step_scratch_ptr(void* stream, void** out);
 constexpr size_t kStepScratchBytes = (size_t)8 << 20;
 
 // The decode step with its scratch memory given explicitly (ws, ws_bytes): the
@@ -686,7 +686,7 @@ hm_status mixer_step_impl(const hm_step_args* a, void* ws, size_t ws_bytes, void
                "step needs " + std::to_string(need) + " bytes of scratch, more than the " +
                    std::to_string(kStepScratchBytes) +
                    " of the allocation-free entry point; use hm_mixer_step with a workspace");
-    hm_status s = step_scratch_ptr(&ws);
+    hm_status s = step_scratch_ptr(stream, &ws);
     if (s != HM_OK) return s;
     ws_bytes = kStepScratchBytes;
   }
@@ -769,10 +769,17 @@ struct ScratchAddr {
 };
 static ScratchAddr g_scratch[kMaxDevices];
 
-hm_status step_scratch_ptr(void** out) {
+hm_status step_scratch_ptr(void* stream, void** out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
     return hm::fail(HM_ERR_HIP, "hipGetDevice failed or device index >= 64");
+  // the array is the current device's, so the kernels must run there
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess || sdev != dev)
+      return hm::fail(HM_ERR_INVALID,
+                      "stream does not belong to the calling thread's current device");
+  }
   ScratchAddr& s = g_scratch[dev];
   // once per device, with that device current (the calling thread's device)
   std::call_once(s.once, [&s]() {

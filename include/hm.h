@@ -385,6 +385,8 @@ size_t hm_mixer_step_workspace(const hm_step_args* a);
  * contents: calls that may overlap on one GPU (different streams without
  * ordering, several host threads) race and must not be used; calls ordered
  * on one stream are fine.  No part of the array needs clearing between calls.
+ * The array is that of the calling thread's current device: a non-NULL
+ * `stream` of another device is rejected (HM_ERR_INVALID, nothing runs).
  * ---------------------------------------------------------------------- */
 hm_status hm_mixer_step_noalloc(const hm_step_args* a, void* stream);
 size_t hm_mixer_step_noalloc_max_bytes(void);
