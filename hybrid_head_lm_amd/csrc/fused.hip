@@ -13,8 +13,11 @@
 //                                             from the aggregates, then runs
 //                                             the chunk (y, final states)
 //   3. branch norm and average
-// The attention is latency bound at well under one workgroup per SIMD and the
-// scan is VALU bound, so the two fill each other's idle issue slots in launch 2.
+// When both parts of a launch are resident at once (a single layer of a few
+// thousand rows) the latency-bound attention and the VALU-bound scan fill each
+// other's idle issue slots; when the scan waves alone fill the chip (long
+// inputs) the launch runs them first and the attention after them, which
+// measured faster than mixing the two on the same CUs.
 // The same device code as the standalone entry points runs in each range.
 #include "attn_dev.h"
 #include "ssm_dev.h"
