@@ -241,4 +241,38 @@ hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, 
   return mark(3);
 }
 
+// The two scan launches of the layer above with no attention work in them:
+// no K/V pre-pass range in the first, no attention range in the second (so
+// the attention arguments are never read).
+hm_status conv_scan_two_launch_bf16(const void* x, const float* cw, const float* cb,
+                                    const float* cst_in, float* cst_out, const void* delta,
+                                    const float* A, const void* Bm, const void* Cm,
+                                    const float* D, const void* z, const float* h0, void* y,
+                                    float* h_out, int B, int T, int Di, void* workspace,
+                                    hipStream_t st) {
+  const int L = scan_chunk_len(B, T, Di);
+  const int nC = (T + L - 1) / L;
+  float* E = (float*)workspace;
+  float* S = E + (size_t)B * nC * kNS * Di;
+  const int gx = (Di + 63) / 64;
+  const PrepGeom pg{0, 1, 1, 0, nullptr, nullptr};
+  const AggGeom ag{gx * (nC - 1) * B, gx, nC > 1 ? nC - 1 : 1, 1};
+  if (ag.n > 0) {
+    hipLaunchKernelGGL(prefill_prep_agg, dim3(ag.n), dim3(64), 0, st, pg, nullptr, nullptr,
+                       nullptr, nullptr, 64, 0LL, 1.0, ag, (const bf16_t*)x,
+                       (const bf16_t*)delta, A, (const bf16_t*)Bm, cw, cb, cst_in, E, S, T, Di,
+                       L, nC);
+    hm_status s = check_launch("prefill_prep_agg (scan aggregates)");
+    if (s != HM_OK) return s;
+  }
+  const FinalGeom fg{gx, (nC + kChunkWaves - 1) / kChunkWaves};
+  const int n_final = fg.gx * fg.nJ * B;
+  hipLaunchKernelGGL(prefill_attn_final, dim3(n_final), dim3(256), 0, st, /*n_attn=*/0, nullptr,
+                     nullptr, nullptr, nullptr, 64, 1, 1, 0, 0, 0LL, 0.f, 1.0, 1, 0, fg,
+                     (const bf16_t*)x, (const bf16_t*)delta, A, (const bf16_t*)Bm,
+                     (const bf16_t*)Cm, D, (const bf16_t*)z, cw, cb, cst_in, cst_out, h0, E, S,
+                     (bf16_t*)y, h_out, T, Di, L, nC, 0);
+  return check_launch("prefill_attn_final (scan final pass)");
+}
+
 }  // namespace hm

@@ -179,6 +179,15 @@ hm_status conv_scan_impl(const void* x, const float* conv_w, const float* conv_b
 // validated every argument.
 bool prefill_fusable(const hm_prefill_args* a);
 hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, hipStream_t st);
+// The bf16 conv + selective scan in two launches (fused.hip): the aggregate
+// pass, then the final pass whose workgroups compose their own incoming
+// states; rows and bases 16-byte aligned (Di % 8 == 0), arguments validated.
+hm_status conv_scan_two_launch_bf16(const void* x, const float* cw, const float* cb,
+                                    const float* cst_in, float* cst_out, const void* delta,
+                                    const float* A, const void* Bm, const void* Cm,
+                                    const float* D, const void* z, const float* h0, void* y,
+                                    float* h_out, int B, int T, int Di, void* workspace,
+                                    hipStream_t st);
 hm_status norm_mean_impl(const void* ya, const void* ys, const float* beta_a,
                          const float* beta_s, float eps, void* out, long long rows,
                          int width, hm_dtype dtype, hipStream_t st, bool dry);
