@@ -62,7 +62,7 @@ COPY_BYTES = 256 << 20      # calibration copy for the HBM byte counters
 ATTN_SOURCES = ("hybrid_head_lm_amd/csrc/attn_dev.h", "hybrid_head_lm_amd/csrc/attn.hip",
                 "hybrid_head_lm_amd/csrc/hm_common.h")
 SSM_SOURCES = ("hybrid_head_lm_amd/csrc/ssm_dev.h", "hybrid_head_lm_amd/csrc/ssm.hip",
-               "hybrid_head_lm_amd/csrc/hm_common.h")
+               "hybrid_head_lm_amd/csrc/fused.hip", "hybrid_head_lm_amd/csrc/hm_common.h")
 STEP_SOURCES = ("hybrid_head_lm_amd/csrc/step.hip", "hybrid_head_lm_amd/csrc/hm_common.h")
 FUSED_SOURCES = ("hybrid_head_lm_amd/csrc/fused.hip", "hybrid_head_lm_amd/csrc/attn_dev.h",
                  "hybrid_head_lm_amd/csrc/ssm_dev.h", "hybrid_head_lm_amd/csrc/hm_common.h")
