@@ -241,6 +241,17 @@ hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, 
   return mark(3);
 }
 
+// Scans whose aggregate waves fill half the chip: there the final pass
+// composing its own incoming states beats a separate carry launch (459 -> 430
+// us at 2 x 16512 rows); on a short scan it saves nothing (45 us either way
+// at 2176 rows) and reads the chunk maps once per final workgroup (105
+// against 79 MB), so the carry launch stays.
+bool conv_scan_two_launch_pays(int B, int T, int Di) {
+  const int L = scan_chunk_len(B, T, Di);
+  const int nC = (T + L - 1) / L;
+  return (long long)((Di + 63) / 64) * (nC - 1) * B >= kAggFirstWaves;
+}
+
 // The two scan launches of the layer above with no attention work in them:
 // no K/V pre-pass range in the first, no attention range in the second (so
 // the attention arguments are never read).

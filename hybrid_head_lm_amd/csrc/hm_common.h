@@ -182,6 +182,8 @@ hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, 
 // The bf16 conv + selective scan in two launches (fused.hip): the aggregate
 // pass, then the final pass whose workgroups compose their own incoming
 // states; rows and bases 16-byte aligned (Di % 8 == 0), arguments validated.
+// conv_scan_two_launch_pays: whether the scan is long enough for that form.
+bool conv_scan_two_launch_pays(int B, int T, int Di);
 hm_status conv_scan_two_launch_bf16(const void* x, const float* cw, const float* cb,
                                     const float* cst_in, float* cst_out, const void* delta,
                                     const float* A, const void* Bm, const void* Cm,

@@ -176,10 +176,10 @@ hm_status conv_scan_impl(const void* x, const float* conv_w, const float* conv_b
              HM_ERR_WORKSPACE, "workspace smaller than hm_selective_scan_workspace()");
   if (dry) return HM_OK;
   if (dtype == HM_BF16) {
-    // aligned bf16 rows: two launches (the final pass composes its own
-    // incoming states) instead of aggregate, carry and final
+    // long scans with aligned bf16 rows: two launches (the final pass
+    // composes its own incoming states) instead of aggregate, carry and final
     if (fuse_conv && Di % 8 == 0 && aligned16(x) && aligned16(delta) && aligned16(Bm) &&
-        aligned16(Cm) && (z == nullptr || aligned16(z)))
+        aligned16(Cm) && (z == nullptr || aligned16(z)) && conv_scan_two_launch_pays(B, T, Di))
       return conv_scan_two_launch_bf16(x, conv_w, conv_b, conv_state_in, conv_state_out, delta,
                                        A, Bm, Cm, D, z, h0, y, h_out, B, T, Di, workspace, st);
     if (fuse_conv)

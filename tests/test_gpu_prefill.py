@@ -212,10 +212,14 @@ def test_selective_scan(shape, use_h0, use_dz):
 
 
 @pytest.mark.parametrize("shape", [TINY, with_(SWA_PREFILL, N=2048, M=128),
-                                   with_(SWA_PREFILL, B=2, N=500, M=7, Di=320, Hq=5)],
-                         ids=["tiny-f32", "swa-full", "ragged"])
+                                   with_(SWA_PREFILL, B=2, N=500, M=7, Di=320, Hq=5),
+                                   with_(SWA_PREFILL, B=4, N=1920, M=128)],
+                         ids=["tiny-f32", "swa-full", "ragged", "long-two-launch"])
 @pytest.mark.parametrize("use_state", [False, True])
 def test_conv_selective_scan(shape, use_state):
+    """The last shape (4 x 2048 rows, 4200 aggregate waves) takes the two-launch
+    form whose final pass composes its own incoming states; the others the
+    aggregate, carry and final launches."""
     inp, h0 = _scan_inputs(shape, 6)
     rng = np.random.default_rng(7)
     cs0 = rng.standard_normal((shape.B, shape.Di, 3)).astype(np.float32) if use_state else None
