@@ -251,7 +251,7 @@ def counter_summaries(c: Counters):
                      "attention q, o and prepared K/V (bf16) + the final scan's x, delta, z read and y "
                      "written (2 B each per token-channel) and B, C (2 B per token-state)",
                      attn_bytes(shape) + bench.scan_bytes(shape))
-    for nm, shape, grid in (("swa-prefill-b1-t2176", SWA_PREFILL, 221440),
+    for nm, shape, grid in (("swa-prefill-b1-t2176", SWA_PREFILL, 223232),
                             ("global-prefill-b4-t8320", GLOBAL_PREFILL, 1925120)):
         write_single(c, f"prefill_attn_final.{nm}.pmc.txt",
                      f"HBM traffic and issue counters of prefill_attn_final (attention | final scan pass) on {nm}",
@@ -311,7 +311,7 @@ def kernel_trace_summary(path, bench_json):
              "#   stack32-b2-t16512 (the step): prefill_prep_agg 913280 (18 layers that prepare K/V) or",
              "#     252800 (14 that reuse it), prefill_attn_final 1914880 (29 window + 3 global",
              "#     layers: the window layers' launches are the shorter ones), norm_mean_rows 2113536",
-             "#   swa-prefill-b1-t2176: prefill_prep_agg 150720, prefill_attn_final 221440,",
+             "#   swa-prefill-b1-t2176: prefill_prep_agg 150720, prefill_attn_final 223232,",
              "#     norm_mean_rows 139264; attn_fwd_bf16 112640 (attention alone); two-stream layer:",
              "#     attn_prep_bf16, attn_fwd_bf16, scan_chunk, scan_carry; cached meta rows: 144320 /",
              "#     204800 / 131072",

@@ -79,6 +79,8 @@ static_assert(kChunkWaves * kNS * 64 * 4 <= kAttnLds, "incoming states fit the r
 
 struct FinalGeom {
   int gx, nJ;   // 64-channel groups; workgroups per group and batch (kChunkWaves chunks each)
+  int n;        // final-pass workgroups (gx * nJ * B); the grid rounds them up to a
+                // multiple of 8 so that the attention ids keep their XCD (id % 8)
 };
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void
@@ -105,6 +107,7 @@ prefill_attn_final(int n_attn, const bf16_t* __restrict__ q, const bf16_t* __res
     return;
   }
   bid = n_fin - 1 - bid;
+  if (bid >= fg.n) return;                      // padding to a multiple of 8
   const int gxi = bid % fg.gx, jw = (bid / fg.gx) % fg.nJ, b = bid / (fg.gx * fg.nJ);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -221,8 +224,9 @@ hm_status prefill_fused_bf16(const hm_prefill_args* a, void* kv, void* scan_ws, 
   const int n_qt = (T + kBM - 1) / kBM;          // query tiles over the token rows
   const int n_groups = B * Hkv * n_qt;
   const int n_attn = 8 * ((n_groups + 7) / 8) * (Hq / Hkv);
-  const FinalGeom fg{gx, (nC + kChunkWaves - 1) / kChunkWaves};
-  const int n_final = fg.gx * fg.nJ * B;
+  const int nJ = (nC + kChunkWaves - 1) / kChunkWaves;
+  const FinalGeom fg{gx, nJ, gx * nJ * B};
+  const int n_final = 8 * ((fg.n + 7) / 8);
   hipLaunchKernelGGL(prefill_attn_final, dim3(n_attn + n_final), dim3(256), 0, st, n_attn,
                      (const bf16_t*)a->q, (const bf16_t*)Kr, (const bf16_t*)Vt, (bf16_t*)a->ya,
                      Tpad, Hq, Hkv, a->n_meta, a->window, a->pos0, scale * kLog2e, rstep, n_qt,
@@ -276,8 +280,9 @@ hm_status conv_scan_two_launch_bf16(const void* x, const float* cw, const float*
     hm_status s = check_launch("prefill_prep_agg (scan aggregates)");
     if (s != HM_OK) return s;
   }
-  const FinalGeom fg{gx, (nC + kChunkWaves - 1) / kChunkWaves};
-  const int n_final = fg.gx * fg.nJ * B;
+  const int nJ = (nC + kChunkWaves - 1) / kChunkWaves;
+  const FinalGeom fg{gx, nJ, gx * nJ * B};
+  const int n_final = 8 * ((fg.n + 7) / 8);
   hipLaunchKernelGGL(prefill_attn_final, dim3(n_final), dim3(256), 0, st, /*n_attn=*/0, nullptr,
                      nullptr, nullptr, nullptr, 64, 1, 1, 0, 0, 0LL, 0.f, 1.0, 1, 0, fg,
                      (const bf16_t*)x, (const bf16_t*)delta, A, (const bf16_t*)Bm,
