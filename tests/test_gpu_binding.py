@@ -82,3 +82,36 @@ def test_step_plan_rejects_mis_sized_tensors():
         hm.StepPlan(dict(layer, ssm_state=_z(B, Di, 8)), kc, kc, 3, M, W)
     with pytest.raises(ValueError, match="k_new"):
         hm.StepPlan(dict(layer, k_new=_z(B, Hkv, Dh + 1), v_new=_z(B, Hkv, Dh)), kc, kc, 3, M, W)
+
+
+def test_prefill_and_block_plans_reject_mis_sized_tensors():
+    bf = torch.bfloat16
+    B, T, Hq, Hkv, Dh, N, M, W = 1, 64, 2, 1, 64, 16, 4, 16
+    Di = Hq * Dh
+    t = {"q": _z(B, T, Hq, Dh, dtype=bf), "k": _z(B, T, Hkv, Dh, dtype=bf),
+         "v": _z(B, T, Hkv, Dh, dtype=bf), "x": _z(B, T, Di, dtype=bf),
+         "delta": _z(B, T, Di, dtype=bf), "Bm": _z(B, T, N, dtype=bf), "Cm": _z(B, T, N, dtype=bf),
+         "z": _z(B, T, Di, dtype=bf), "A": _z(Di, N), "D": _z(Di), "conv_w": _z(Di, 4),
+         "conv_b": _z(Di), "beta_a": _z(Di), "beta_s": _z(Di)}
+    with pytest.raises(ValueError, match="z"):
+        hm.PrefillPlan(dict(t, z=_z(B, T - 1, Di, dtype=bf)), M, W)
+    with pytest.raises(ValueError, match="beta_s"):
+        hm.PrefillPlan(dict(t, beta_s=_z(Di + 1)), M, W)
+    with pytest.raises(ValueError, match="meta k"):
+        hm.PrefillPlan(t, M, W, meta={"k": _z(M + 1, Hkv, Dh, dtype=bf),
+                                      "v": _z(M, Hkv, Dh, dtype=bf)})
+    with pytest.raises(ValueError, match="out"):
+        hm.PrefillPlan(t, M, W, out=_z(B, T, Di - 1, dtype=bf))
+    d_model, d_ffn = 128, 192
+    w = {"ln1": _z(d_model), "ln2": _z(d_model),
+         "w_in": _z(Hq * Dh + 2 * Hkv * Dh + 2 * Di, d_model, dtype=bf),
+         "w_dbc": _z(Di + 2 * N, Di, dtype=bf), "dt_bias": _z(Di), "A": _z(Di, N), "D": _z(Di),
+         "conv_w": _z(Di, 4), "conv_b": _z(Di), "beta_a": _z(Di), "beta_s": _z(Di),
+         "w_out": _z(d_model, Di, dtype=bf), "w_up": _z(d_ffn, d_model, dtype=bf),
+         "w_down": _z(d_model, d_ffn, dtype=bf)}
+    hidden = _z(B, T, d_model, dtype=bf)
+    with pytest.raises(ValueError, match="w_in"):
+        # a block that reuses its neighbour's K/V has no K, V rows in w_in
+        hm.BlockPlan(w, hidden, Hq, Hkv, M, W, kv=_z(1 << 20, dtype=torch.uint8), kv_reuse=True)
+    with pytest.raises(ValueError, match="w_down"):
+        hm.BlockPlan(dict(w, w_down=_z(d_model, d_ffn - 64, dtype=bf)), hidden, Hq, Hkv, M, W)
