@@ -85,6 +85,16 @@ def test_decode_pair_bf16_global(n_prev):
     _check(shape, 11 + n_prev)
 
 
+@pytest.mark.parametrize("M,W,n_prev", [(5, 100, 0), (5, 100, 99), (5, 100, 100), (5, 100, 350),
+                                         (63, 65, 64), (1, 127, 500)])
+def test_decode_pair_bf16_unaligned_window(M, W, n_prev):
+    """Meta and window lengths off the 64-row tile grid: the visible rows end
+    inside a tile, and the ring slot wraps at a window that is not a tile
+    multiple."""
+    shape = with_(DECODE_PAIR, B=4, M=M, W=W, cache_slots=W, n_prev=n_prev)
+    _check(shape, 31 + n_prev)
+
+
 def test_decode_pair_bf16_global_long_cache():
     """A global layer with a long cache: more key splits than the combine keeps
     in registers."""
